@@ -1,0 +1,153 @@
+"""Pure-Python model of the paged KV block pool -- TEST INFRASTRUCTURE.
+
+Used only by the tests, to compare the native allocator bit for bit (block
+tables, slot mappings, lengths, refcounts and the free list) after every
+operation of random traces.  It shares no code with the library.
+
+What the pages fix, and where:
+  * K/V live in fixed-size physical blocks (16 tokens by default) in one pool;
+    a per-sequence block table maps logical block i to a physical block, and
+    physical placement is irrelevant ([cf1] www.cf-1.com/news/5824798, §3.1).
+  * Blocks are taken from a global free list on demand, when the current
+    block is full; only the last block of a sequence can be partly filled
+    ([cf1] §3.2).  Pre-allocation makes an append a mere index move
+    ([moo] www.mooersco.com/news/1484987, §2.2).
+  * Several block tables may point at the same physical blocks (shared
+    prefix, beam search, parallel sampling); a block is reclaimed when nobody
+    references it ([cf1] §2.3, §3.3; [lqnn] m.lqnn.cn/news/219451, §3).
+
+What the pages leave open, and the reading taken here:
+  * Free-list order: a FIFO deque seeded from a caller-given order; allocation
+    pops the front, release pushes to the back, a sequence's blocks in logical
+    order.
+  * Sharing is of whole blocks only: a fork shares the first n/bs blocks and
+    needs n % bs == 0 (partial-block copy-on-write is not modelled).
+  * Reserve is all-or-nothing: without enough free blocks nothing changes.
+  * Slot of logical position p: table[p // bs] * bs + p % bs.
+"""
+from __future__ import annotations
+
+from collections import deque
+
+OK, INVALID_ARG, NO_BLOCKS, OUT_OF_RANGE, STATE = 0, 1, 2, 3, 4
+INT32_MAX = 2**31 - 1
+
+
+class AllocError(Exception):
+    def __init__(self, code: int, msg: str = ""):
+        super().__init__(msg or str(code))
+        self.code = code
+
+
+class BlockPoolModel:
+    def __init__(self, num_blocks: int, block_size: int = 16, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise AllocError(INVALID_ARG, "num_blocks and block_size must be > 0")
+        order = list(range(num_blocks)) if free_order is None else [int(x) for x in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise AllocError(INVALID_ARG, "free order must be a permutation of 0..N-1")
+        self.N = num_blocks
+        self.bs = block_size
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+        self.seqs = {}          # id -> [blocks list, length]
+        self.next_id = 0
+
+    # -- sequences -------------------------------------------------------
+    def seq_create(self) -> int:
+        sid = self.next_id
+        self.next_id += 1
+        self.seqs[sid] = [[], 0]
+        return sid
+
+    def _get(self, sid):
+        if sid not in self.seqs:
+            raise AllocError(STATE, f"unknown or freed sequence {sid}")
+        return self.seqs[sid]
+
+    def reserve(self, sid: int, n: int):
+        """Append n token positions; return their slots."""
+        s = self._get(sid)
+        if n < 0:
+            raise AllocError(INVALID_ARG, "n_tokens < 0")
+        blocks, length = s
+        new_len = length + n
+        if new_len > INT32_MAX:
+            raise AllocError(OUT_OF_RANGE, "sequence length overflow")
+        need = -(-new_len // self.bs) - len(blocks)
+        if need > len(self.free):
+            raise AllocError(NO_BLOCKS, "not enough free blocks")
+        if n > 0 and length % self.bs != 0 and self.ref[blocks[-1]] != 1:
+            raise AllocError(STATE, "would write into a shared block")
+        for _ in range(need):
+            b = self.free.popleft()
+            assert self.ref[b] == 0
+            self.ref[b] = 1
+            blocks.append(b)
+        slots = [blocks[p // self.bs] * self.bs + p % self.bs for p in range(length, new_len)]
+        s[1] = new_len
+        return slots
+
+    def fork(self, parent: int, n_shared: int) -> int:
+        p = self._get(parent)
+        if n_shared < 0 or n_shared > p[1] or n_shared % self.bs != 0:
+            raise AllocError(INVALID_ARG, "fork length must be block aligned and <= parent length")
+        shared = p[0][: n_shared // self.bs]
+        for b in shared:
+            self.ref[b] += 1
+        sid = self.seq_create()
+        self.seqs[sid] = [list(shared), n_shared]
+        return sid
+
+    def free_seq(self, sid: int) -> None:
+        blocks, _ = self._get(sid)
+        for b in blocks:
+            self.ref[b] -= 1
+            assert self.ref[b] >= 0
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.seqs[sid]
+
+    # -- queries -----------------------------------------------------------
+    def length(self, sid: int) -> int:
+        return self._get(sid)[1]
+
+    def table(self, sid: int):
+        return list(self._get(sid)[0])
+
+    def tables(self, sids, max_blocks: int):
+        rows, lens = [], []
+        for sid in sids:
+            blocks, length = self._get(sid)
+            if len(blocks) > max_blocks:
+                raise AllocError(OUT_OF_RANGE, "table wider than max_blocks_per_seq")
+            rows.append(blocks + [-1] * (max_blocks - len(blocks)))
+            lens.append(length)
+        return rows, lens
+
+    def refcount(self, block: int) -> int:
+        if not 0 <= block < self.N:
+            raise AllocError(INVALID_ARG, "block out of range")
+        return self.ref[block]
+
+    def free_list(self):
+        return list(self.free)
+
+    def shared_blocks(self) -> int:
+        return sum(1 for r in self.ref if r > 1)
+
+    # -- invariants ([cf1] §3.2, §3.3) ----------------------------------------
+    def check_invariants(self) -> None:
+        holders = [0] * self.N
+        for blocks, length in self.seqs.values():
+            assert len(blocks) == -(-length // self.bs), "blocks != ceil(len / bs)"
+            for b in blocks:
+                holders[b] += 1
+        free_set = set(self.free)
+        assert len(free_set) == len(self.free), "a block is in the free list twice"
+        for b in range(self.N):
+            if b in free_set:
+                assert self.ref[b] == 0 and holders[b] == 0
+            else:
+                assert self.ref[b] == holders[b] and self.ref[b] > 0, f"refcount mismatch on {b}"
+        assert len(self.free) + sum(1 for r in self.ref if r > 0) == self.N

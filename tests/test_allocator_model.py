@@ -1,0 +1,110 @@
+"""Pins of the Python block-pool model (CPU only): page numbers and invariants."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle.allocator_model import (NO_BLOCKS, INVALID_ARG, STATE, OUT_OF_RANGE, AllocError,
+                                    BlockPoolModel)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_block_counts_printed_on_pages():
+    with open(os.path.join(GOLDEN, "block_counts.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        m = BlockPoolModel(c["blocks"] + 3, g["block_size"])
+        s = m.seq_create()
+        m.reserve(s, c["tokens"])
+        assert len(m.table(s)) == c["blocks"], c["cite"]
+        m.check_invariants()
+
+
+def test_on_demand_growth_one_block_per_16_tokens():
+    # cf-1.com/news/5824798 §3.2: a new block only when the current one is full
+    m = BlockPoolModel(8, 16, free_order=[5, 2, 7, 0, 1, 3, 4, 6])
+    s = m.seq_create()
+    slots = []
+    for _ in range(33):
+        slots += m.reserve(s, 1)
+    assert m.table(s) == [5, 2, 7]
+    assert slots[:16] == [5 * 16 + i for i in range(16)]
+    assert slots[16:32] == [2 * 16 + i for i in range(16)]
+    assert slots[32] == 7 * 16
+    assert m.free_list() == [0, 1, 3, 4, 6]
+
+
+def test_shared_prefix_is_stored_once():
+    # cf-1.com/news/5824798 §2.3 and §3.3: a 2048-token system prompt shared by 16
+    # requests is kept once; every table points at the same physical blocks
+    m = BlockPoolModel(128 + 16 * 10, 16)
+    owner = m.seq_create()
+    m.reserve(owner, 2048)
+    kids = [m.fork(owner, 2048) for _ in range(15)]
+    prefix = m.table(owner)
+    assert all(m.table(k) == prefix for k in kids)
+    assert all(m.refcount(b) == 16 for b in prefix)
+    for k in [owner] + kids:
+        m.reserve(k, 100)
+    used = m.N - len(m.free_list())
+    assert used == 128 + 16 * 7            # prefix once + ceil(100/16) own blocks each
+    assert m.shared_blocks() == 128
+    m.check_invariants()
+    for k in kids:
+        m.free_seq(k)
+    assert all(m.refcount(b) == 1 for b in prefix)
+    m.free_seq(owner)
+    assert len(m.free_list()) == m.N
+    m.check_invariants()
+
+
+def test_errors_and_atomic_reserve():
+    m = BlockPoolModel(4, 16)
+    s = m.seq_create()
+    m.reserve(s, 40)                                  # 3 blocks
+    before = (m.table(s), m.length(s), m.free_list())
+    with pytest.raises(AllocError) as e:
+        m.reserve(s, 40)                              # needs 3 more, 1 free
+    assert e.value.code == NO_BLOCKS
+    assert (m.table(s), m.length(s), m.free_list()) == before
+    with pytest.raises(AllocError) as e:
+        m.fork(s, 20)
+    assert e.value.code == INVALID_ARG
+    with pytest.raises(AllocError) as e:
+        m.fork(s, 48)
+    assert e.value.code == INVALID_ARG
+    with pytest.raises(AllocError) as e:
+        m.tables([s], 2)
+    assert e.value.code == OUT_OF_RANGE
+    m.free_seq(s)
+    with pytest.raises(AllocError) as e:
+        m.free_seq(s)
+    assert e.value.code == STATE
+    with pytest.raises(AllocError) as e:
+        BlockPoolModel(4, 16, free_order=[0, 1, 1, 2])
+    assert e.value.code == INVALID_ARG
+
+
+def test_random_traces_keep_invariants():
+    rng = np.random.default_rng(0)
+    for trial in range(20):
+        n = int(rng.integers(8, 65))
+        m = BlockPoolModel(n, 16, free_order=rng.permutation(n))
+        live = []
+        for _ in range(500):
+            op = rng.integers(0, 4)
+            try:
+                if op == 0 or not live:
+                    live.append(m.seq_create())
+                elif op == 1:
+                    m.reserve(live[rng.integers(len(live))], int(rng.integers(0, 40)))
+                elif op == 2:
+                    p = live[rng.integers(len(live))]
+                    live.append(m.fork(p, 16 * int(rng.integers(0, m.length(p) // 16 + 1))))
+                else:
+                    m.free_seq(live.pop(rng.integers(len(live))))
+            except AllocError as e:
+                assert e.code == NO_BLOCKS
+            m.check_invariants()

@@ -1,0 +1,66 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies oracle/oracle.c, plants one plausible mistake by text
+substitution (a dropped term, a wrong sign or index, a swapped operand),
+compiles the copy with gcc into a temporary directory and runs the pins of
+tests/test_oracle_pins.py against it.  At least one pin must fail.  The real
+oracle is untouched; the mutants only ever run on the CPU.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "kv_formula_drops_factor_2": ("(uint64_t)2 *", "(uint64_t)1 *", [pins.check_kv_sizes]),
+    "f16_exponent_bias_off_by_one": ("e - 25", "e - 24", [pins.check_f16_widen]),
+    "bf16_shift_wrong": ("(uint32_t)b << 16", "(uint32_t)b << 15", [pins.check_bf16_widen]),
+    "e4m3_subnormal_scale": ("ldexp((double)m, -9)", "ldexp((double)m, -10)", [pins.check_e4m3_decode]),
+    "e4m3_normal_bias": ("e - 10);", "e - 11);", [pins.check_e4m3_decode]),
+    "e4m3_ties_always_down": ("(lo % 2 == 0) ? lo : hi", "lo", [pins.check_e4m3_encode]),
+    "e4m3_overflow_to_nan": ("if (a >= 448.0) return (uint8_t)(sign | 0x7E);",
+                             "if (a >= 449.0) return 0x7F;", [pins.check_e4m3_encode]),
+    "gqa_interleaved_heads": ("const int32_t h = g * G + hh;", "const int32_t h = hh * H_kv + g;",
+                              [pins.check_gqa_equals_repeated_mha, pins.check_attention_textbook]),
+    "drop_newest_token": ("j < n;", "j < n - 1;",
+                          [pins.check_attention_textbook, pins.check_cached_decode_equals_recompute]),
+    "logits_read_values": ("widen(K, kv_dtype, kbase + i)", "widen(V, kv_dtype, kbase + i)",
+                           [pins.check_attention_textbook]),
+    "keys_reversed": ("const int64_t kbase = ((tok_off[b] + j)",
+                      "const int64_t kbase = ((tok_off[b] + (n - 1 - j))",
+                      [pins.check_attention_textbook, pins.check_attention_closed_forms]),
+    "softmax_sign": ("exp(z[j] - m)", "exp(m - z[j])", [pins.check_attention_textbook]),
+    "scale_dropped": ("z[j] = s * dot;", "z[j] = dot;", [pins.check_attention_textbook]),
+    "no_normalisation": ("o[i] /= l;", "o[i] /= 1.0;",
+                         [pins.check_attention_textbook, pins.check_attention_closed_forms]),
+    "fp8_key_scale_dropped": ("* (widen(K, kv_dtype, kbase + i) * ks)", "* widen(K, kv_dtype, kbase + i)",
+                              [pins.check_fp8_attention_on_dequantised_values]),
+    "fp8_value_scale_dropped": ("(widen(V, kv_dtype, vbase + i) * vs)", "widen(V, kv_dtype, vbase + i)",
+                                [pins.check_fp8_attention_on_dequantised_values]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path, monkeypatch):
+    find, repl, checks = MUTANTS[name]
+    with open(SRC) as f:
+        src = f.read()
+    assert find in src, f"mutation site vanished: {find!r}"
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(src.replace(find, repl))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    str(mutant), "-o", str(so), "-lm"], check=True)
+    monkeypatch.setattr(oracle, "_lib", oracle.bind(str(so)))
+    caught = []
+    for check in checks:
+        try:
+            check()
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"planted mistake {name!r} passed every pin"

@@ -1,0 +1,324 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Every check here compares the oracle with a number a page prints, a library
+routine of a different formulation, a specification constant or a closed
+form.  The checks are plain functions (``check_*``) so that the planted-
+mistake tests can run them against deliberately broken oracle builds.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# KV size formula
+# ---------------------------------------------------------------------------
+def check_kv_sizes():
+    g = _golden("kv_sizes.json")
+    for e in g["exact"]:
+        got = oracle.kv_cache_bytes(e["layers"], e["kv_heads"], e["head_dim"], e["elem_bytes"],
+                                    e["tokens"], e["seqs"])
+        assert got == e["bytes"], (e["cite"], got)
+    for e in g["approx"]:
+        got = oracle.kv_cache_bytes(e["layers"], e["kv_heads"], e["head_dim"], e["elem_bytes"],
+                                    e["tokens"], e["seqs"])
+        assert abs(got - e["printed"]) <= e["rel_tol"] * e["printed"], (e["cite"], got)
+    b = g["budget"]
+    per_tok = oracle.kv_cache_bytes(b["layers"], b["kv_heads"], b["head_dim"], b["elem_bytes"], 1, 1)
+    tokens = (b["budget_gib"] * 1024**3) // per_tok
+    assert tokens == b["tokens"]
+    assert tokens // 4096 == b["requests_at_4096"]
+
+
+def test_kv_sizes_printed_on_pages():
+    check_kv_sizes()
+
+
+def test_kv_sizes_reject_invalid_shapes():
+    # the budget script on m.lqnn.cn/news/219451 §2 refuses non-positive structure
+    assert oracle.kv_cache_bytes(0, 8, 128, 2, 1, 1) == 0
+    assert oracle.kv_cache_bytes(32, 8, 128, 0, 1, 1) == 0
+    assert oracle.kv_cache_bytes(32, 8, 128, 2, -1, 1) == 0
+    assert oracle.kv_cache_bytes(32, 8, 128, 2, 0, 1) == 0
+
+
+# ---------------------------------------------------------------------------
+# Exact widening of stored values
+# ---------------------------------------------------------------------------
+def check_f16_widen():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.widen(bits.view(np.float16), oracle.F16)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def check_bf16_widen():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.widen(bits, oracle.BF16)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_f16_widen_all_patterns():
+    check_f16_widen()
+
+
+def test_bf16_widen_all_patterns():
+    check_bf16_widen()
+
+
+# ---------------------------------------------------------------------------
+# OCP E4M3 codec
+# ---------------------------------------------------------------------------
+def _torch_e4m3_decode():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float32).to(torch.float64).numpy()
+
+
+def check_e4m3_decode():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.widen(codes, oracle.E4M3)
+    ref = _torch_e4m3_decode()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # specification constants: bias 7, max 448, min subnormal 2^-9, min normal 2^-6,
+    # S.1111.111 is NaN and there are no infinities
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0**-9 and got[0x08] == 2.0**-6
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and nan.sum() == 2
+    assert not np.isinf(got).any()
+    assert got[0x38] == 1.0                       # exponent field 7 = bias
+
+
+def test_e4m3_decode_all_codes():
+    check_e4m3_decode()
+
+
+def _e4m3_critical_inputs():
+    """Every midpoint between neighbouring codes, one float ulp either side,
+    the codes themselves, plus random floats inside the finite range."""
+    pos = oracle.widen(np.arange(127, dtype=np.uint8), oracle.E4M3)     # 0 .. 448
+    mids = (pos[:-1] + pos[1:]) / 2
+    m32 = mids.astype(np.float32)
+    assert np.array_equal(m32.astype(np.float64), mids)                 # midpoints are floats
+    xs = [pos.astype(np.float32), m32,
+          np.nextafter(m32, np.float32(np.inf)), np.nextafter(m32, np.float32(-np.inf))]
+    rng = np.random.default_rng(7)
+    xs.append(rng.uniform(0, 448, 200000).astype(np.float32))
+    xs.append((rng.uniform(0, 1, 200000) * 2.0**rng.integers(-24, 0, 200000)).astype(np.float32))
+    x = np.concatenate(xs)
+    return np.concatenate([x, -x])
+
+
+def check_e4m3_encode():
+    x = _e4m3_critical_inputs()
+    got = oracle.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:10]
+    # encode(decode(c)) == c on every finite code (+0 and -0 included)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = oracle.widen(codes, oracle.E4M3).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_encode(vals), codes)
+    # saturation beyond the largest finite value (outliers saturate), NaN code
+    big = np.array([448.0, 449.0, 464.0, 480.0, 1e6, np.inf, 3.4e38], np.float32)
+    assert np.all(oracle.e4m3_encode(big) == 0x7E)
+    assert np.all(oracle.e4m3_encode(-big) == 0xFE)
+    assert oracle.e4m3_encode(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+def test_e4m3_encode_rne_saturating():
+    check_e4m3_encode()
+
+
+# ---------------------------------------------------------------------------
+# Decode attention
+# ---------------------------------------------------------------------------
+def _textbook(q64, K64, V64, tok_off, lens, scale):
+    """softmax(scale * q K^T) V per (b, h) with scipy's softmax and numpy matmul."""
+    B, H_q, D = q64.shape
+    H_kv = K64.shape[1]
+    G = H_q // H_kv
+    out = np.zeros((B, H_q, D))
+    for b in range(B):
+        n = int(lens[b])
+        if n <= 0:
+            continue
+        for h in range(H_q):
+            g = h // G
+            Kb = K64[tok_off[b]:tok_off[b] + n, g, :]
+            Vb = V64[tok_off[b]:tok_off[b] + n, g, :]
+            w = scipy.special.softmax(np.float64(np.float32(scale)) * (Kb @ q64[b, h]))
+            out[b, h] = w @ Vb
+    return out
+
+
+def _random_case(seed, B, H_q, H_kv, D, lens, dtype):
+    rng = np.random.default_rng(seed)
+    T = int(np.sum(lens))
+    tok_off = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    q = wl.cast_to_storage(rng.standard_normal((B, H_q, D)).astype(np.float32), dtype)
+    K = wl.cast_to_storage(rng.standard_normal((T, H_kv, D)).astype(np.float32), dtype)
+    V = wl.cast_to_storage(rng.standard_normal((T, H_kv, D)).astype(np.float32), dtype)
+    return q, K, V, tok_off, np.asarray(lens, np.int32)
+
+
+def check_attention_textbook():
+    cases = [(11, 3, 8, 2, 16, [1, 7, 33], oracle.F32, 0.25),
+             (12, 2, 5, 1, 32, [16, 40], oracle.F16, 1 / math.sqrt(32)),
+             (13, 2, 6, 3, 8, [5, 18], oracle.BF16, 0.7)]
+    for seed, B, Hq, Hkv, D, lens, dt, scale in cases:
+        q, K, V, off, ln = _random_case(seed, B, Hq, Hkv, D, lens, dt)
+        got = oracle.decode_attention(q, dt, K, V, dt, off, ln, scale)
+        ref = _textbook(oracle.widen(q, dt), oracle.widen(K, dt), oracle.widen(V, dt), off, ln, scale)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_vs_textbook_softmax():
+    check_attention_textbook()
+
+
+def check_attention_closed_forms():
+    rng = np.random.default_rng(3)
+    D = 16
+    # single-token context: the weight is exactly 1, out = V_0 exactly
+    q = rng.standard_normal((1, 2, D)).astype(np.float32)
+    K = rng.standard_normal((1, 2, D)).astype(np.float32)
+    V = rng.standard_normal((1, 2, D)).astype(np.float32)
+    out = oracle.decode_attention(q, oracle.F32, K, V, oracle.F32, [0], [1], 0.25)
+    assert np.array_equal(out[0], V[0].astype(np.float64))
+    # q = 0: uniform weights, out = mean of V
+    n = 9
+    K = rng.standard_normal((n, 1, D)).astype(np.float32)
+    V = rng.standard_normal((n, 1, D)).astype(np.float32)
+    out = oracle.decode_attention(np.zeros((1, 1, D), np.float32), oracle.F32, K, V, oracle.F32,
+                                  [0], [n], 0.25)
+    np.testing.assert_allclose(out[0, 0], V[:, 0].astype(np.float64).mean(axis=0), atol=1e-14)
+    # constant V: out = that constant
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    Vc = np.full((n, 1, D), 0.375, np.float32)
+    out = oracle.decode_attention(q, oracle.F32, K, Vc, oracle.F32, [0], [n], 0.25)
+    np.testing.assert_allclose(out[0, 0], 0.375, atol=1e-15)
+    # two tokens: out = sigmoid(z0 - z1) V0 + sigmoid(z1 - z0) V1
+    K2 = rng.standard_normal((2, 1, D)).astype(np.float32)
+    V2 = rng.standard_normal((2, 1, D)).astype(np.float32)
+    s = 0.3
+    z = [float(np.float32(s)) * float(np.dot(q[0, 0].astype(np.float64), K2[j, 0].astype(np.float64)))
+         for j in range(2)]
+    sig = lambda t: 1.0 / (1.0 + math.exp(-t))
+    ref = sig(z[0] - z[1]) * V2[0, 0].astype(np.float64) + sig(z[1] - z[0]) * V2[1, 0].astype(np.float64)
+    out = oracle.decode_attention(q, oracle.F32, K2, V2, oracle.F32, [0], [2], s)
+    np.testing.assert_allclose(out[0, 0], ref, atol=1e-14)
+    # one key aligned with q and scaled up: out tends to its value
+    Kl = rng.standard_normal((n, 1, D)).astype(np.float32)
+    Kl[4, 0] = 50.0 * q[0, 0]
+    out = oracle.decode_attention(q, oracle.F32, Kl, V, oracle.F32, [0], [n], 1.0)
+    np.testing.assert_allclose(out[0, 0], V[4, 0].astype(np.float64), atol=1e-12)
+    # empty context: zeros
+    out = oracle.decode_attention(q, oracle.F32, K, V, oracle.F32, [0], [0], 0.25)
+    assert np.array_equal(out, np.zeros_like(out))
+
+
+def test_attention_closed_forms():
+    check_attention_closed_forms()
+
+
+def check_gqa_equals_repeated_mha():
+    # several query heads sharing one KV head (mlqm.cn/news/394450, 六) equals MHA
+    # with each KV head repeated G times, consecutive query heads per group
+    B, Hq, Hkv, D = 2, 10, 2, 16
+    lens = [13, 30]
+    q, K, V, off, ln = _random_case(21, B, Hq, Hkv, D, lens, oracle.F32)
+    gqa = oracle.decode_attention(q, oracle.F32, K, V, oracle.F32, off, ln, 0.25)
+    G = Hq // Hkv
+    Kr = np.repeat(K, G, axis=1)
+    Vr = np.repeat(V, G, axis=1)
+    mha = oracle.decode_attention(q, oracle.F32, Kr, Vr, oracle.F32, off, ln, 0.25)
+    assert np.array_equal(gqa, mha)
+    # and it is not trivially so: a different head->group map gives other values
+    Kalt = np.tile(K, (1, G, 1))
+    Valt = np.tile(V, (1, G, 1))
+    alt = oracle.decode_attention(q, oracle.F32, Kalt, Valt, oracle.F32, off, ln, 0.25)
+    assert not np.allclose(alt, gqa)
+
+
+def test_gqa_equals_repeated_mha():
+    check_gqa_equals_repeated_mha()
+
+
+def check_cached_decode_equals_recompute():
+    # The walk-through on mlqm.cn/news/394450 (四): d_model 64, 4 heads of 16,
+    # 5-token prompt then 3 decode steps, cache 5 -> 8.  Each decode step's output
+    # must equal the last row of full no-cache causal attention over the history.
+    x, Wq, Wk, Wv = wl.mini_model_inputs(seed=99, n_tokens=8)
+    H, dk = 4, 16
+    Q = (x @ Wq).reshape(8, H, dk)
+    Kx = (x @ Wk).reshape(8, H, dk)
+    Vx = (x @ Wv).reshape(8, H, dk)
+    scale = float(np.float32(1 / math.sqrt(dk)))
+    full = oracle.causal_attention(Q, Kx, Vx, scale)
+    for t in range(5, 9):                       # context lengths after prefill / each step
+        # the oracle takes stored values; float32 storage of the projections
+        q32 = Q[t - 1:t].astype(np.float32)
+        K32, V32 = Kx[:t].astype(np.float32), Vx[:t].astype(np.float32)
+        dec = oracle.decode_attention(q32, oracle.F32, K32, V32, oracle.F32, [0], [t], scale)
+        Q32 = Q[:t].astype(np.float32).astype(np.float64)
+        ref = oracle.causal_attention(Q32, K32.astype(np.float64), V32.astype(np.float64), scale)[t - 1]
+        np.testing.assert_allclose(dec[0], ref, atol=1e-12)
+        # and against the recompute from the float64 history (only float32 storage rounding apart)
+        np.testing.assert_allclose(dec[0], full[t - 1], atol=1e-5)
+
+
+def test_cached_decode_equals_recompute():
+    check_cached_decode_equals_recompute()
+
+
+def check_fp8_attention_on_dequantised_values():
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, D, lens = 2, 4, 2, 16, [20, 35]
+    T = sum(lens)
+    off = np.array([0, lens[0]], np.int64)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    codes_k = rng.integers(0, 256, (T, Hkv, D)).astype(np.uint8)
+    codes_v = rng.integers(0, 256, (T, Hkv, D)).astype(np.uint8)
+    codes_k[(codes_k & 0x7F) == 0x7F] = 0x11        # no NaN codes in live data
+    codes_v[(codes_v & 0x7F) == 0x7F] = 0x22
+    ks = np.array([0.03, 0.5], np.float32)
+    vs = np.array([0.25, 0.0078125], np.float32)
+    got = oracle.decode_attention(q, oracle.BF16, codes_k, codes_v, oracle.E4M3, off, lens, 0.25,
+                                  k_scale=ks, v_scale=vs)
+    dec = _torch_e4m3_decode()
+    K64 = dec[codes_k] * ks.astype(np.float64)[None, :, None]
+    V64 = dec[codes_v] * vs.astype(np.float64)[None, :, None]
+    ref = _textbook(wl.bf16_bits_to_f32(q).astype(np.float64), K64, V64, off, lens, 0.25)
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def test_fp8_attention_on_dequantised_values():
+    check_fp8_attention_on_dequantised_values()
+
+
+ALL_CHECKS = [check_kv_sizes, check_f16_widen, check_bf16_widen, check_e4m3_decode,
+              check_e4m3_encode, check_attention_textbook, check_attention_closed_forms,
+              check_gqa_equals_repeated_mha, check_cached_decode_equals_recompute,
+              check_fp8_attention_on_dequantised_values]
