@@ -1,0 +1,209 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+One step = one decode step of the whole batch of one layer: kv_append of every
+sequence's new token, then paged_decode (partition kernel + reduce kernel),
+with the pool, tables, queries and new K/V already resident in device memory.
+The host-side allocator work of a step (reserve one slot per sequence and
+rebuild the block tables) is timed separately on the CPU and reported beside.
+
+Prints one JSON line.  value = algorithmic KV bytes read per step / step time,
+in GB/s (every live K and V element once per sequence).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mha7b]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode KV GB/s (% of HBM peak) and decode tokens/s per layer, 1 MI355X"
+KERNEL_SOURCES = ["paged_kv_cache_152_amd/csrc/decode.hip", "paged_kv_cache_152_amd/csrc/append.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def traffic_for(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def host_alloc_us(w: wl.Workload, reps: int = 20) -> float:
+    """CPU cost of one decode step's bookkeeping (reserve 1 slot per sequence,
+    rebuild the block tables) on a metadata-only pool of the same shape."""
+    import paged_kv_cache_152_amd as pkv
+    pool = pkv.KVPool(w.num_blocks + w.B * (reps + 1), w.H_kv, w.D, w.kv_dtype, host_only=True)
+    seqs = [pool.seq_create() for _ in range(w.B)]
+    for s, n in zip(seqs, w.lens):
+        pool.seq_reserve(s, int(n) - 1)
+    mb = w.max_blocks_per_seq() + reps
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for s in seqs:
+            pool.seq_reserve(s, 1)
+        pool.block_tables(seqs, mb)
+    dt = (time.perf_counter() - t0) / reps
+    pool.close()
+    return dt * 1e6
+
+
+def cpu_baseline(w: wl.Workload, budget_s: float = 15.0):
+    """The fp64 oracle on a bounded sample of the same workload, timed on the host."""
+    import oracle
+    from tests.oracle_ref import fp8_codes
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.B)
+    done_bytes, done_time, used = 0, 0.0, []
+    per_tok = w.H_kv * w.D * 2 * wl.ELEM_BYTES[w.kv_dtype]
+    scales = w.fp8_scales()
+    for b in order:
+        K, V = w.kv(int(b))
+        n = int(w.lens[b])
+        if w.kv_dtype == wl.E4M3:
+            K, V = fp8_codes(K[:n], scales[0]), fp8_codes(V[:n], scales[1])
+        kw = dict(k_scale=scales[0], v_scale=scales[1]) if scales else {}
+        q = w.q()[[int(b)]]
+        t0 = time.perf_counter()
+        oracle.decode_attention(q, w.q_dtype, K[:n], V[:n], w.kv_dtype, [0], [n], w.scale, **kw)
+        done_time += time.perf_counter() - t0
+        done_bytes += n * per_tok
+        used.append(int(b))
+        if done_time >= budget_s:
+            break
+    return {"value": round(done_bytes / done_time / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle over {len(used)} of {w.B} sequences ({done_bytes / 2**30:.2f} GiB of KV, "
+                      f"{done_time:.1f} s); same algorithmic-bytes rate as value"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8"])
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(each GPU would own its own pool and sequences); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import harness
+    import paged_kv_cache_152_amd as pkv
+
+    w = wl.make(args.workload)
+    log(f"[bench] workload {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} D={w.D} "
+        f"kv={wl.DTYPE_NAMES[w.kv_dtype]} blocks={w.num_blocks} tokens={int(w.lens.sum())}")
+    t0 = time.time()
+    prep = harness.prepare(w, partition_tokens=args.partition)
+    torch.cuda.synchronize()
+    log(f"[bench] pool filled in {time.time() - t0:.1f} s")
+    pool = prep.pool
+    out = torch.empty_like(prep.q)
+    ws_bytes = pool.workspace_bytes(w.B, w.H_q, prep.max_len)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    P = pool.partition_tokens(w.B, w.H_q, prep.max_len)
+
+    for _ in range(args.warmup):
+        prep.step(out=out, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps), timing {args.steps} steps")
+
+    pool.profile_enable(True)
+    pool.profile_read()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        prep.step(out=out, workspace=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    stats = pool.profile_read()
+    pool.profile_enable(False)
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    kv_bytes = w.kv_bytes_per_step()
+    kern = {k: {"launches": v["launches"], "avg_us": round(v["total_ms"] / max(1, v["launches"]) * 1e3, 3)}
+            for k, v in stats.items()}
+    part_us = kern.get("paged_decode_partition", {}).get("avg_us")
+    red_us = kern.get("paged_decode_reduce", {}).get("avg_us", 0.0)
+    achieved = kv_bytes / (part_us * 1e-6) / 1e9 if part_us else None
+    traffic = traffic_for(w.name, "paged_decode_partition")
+    result = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.DTYPE_NAMES[w.kv_dtype],
+        "data": "synthetic (seeded N(0,1) K/V and q; block tables from a seeded permutation of the pool)",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.H_q, "kv_heads": w.H_kv, "head_dim": w.D,
+                   "block_size": wl.BLOCK, "kv_dtype": wl.DTYPE_NAMES[w.kv_dtype],
+                   "q_dtype": wl.DTYPE_NAMES[w.q_dtype], "context_min": int(w.lens.min()),
+                   "context_max": int(w.lens.max()), "context_tokens": int(w.lens.sum()),
+                   "pool_blocks": w.num_blocks, "partition_tokens": P, "layers": 1},
+        "decode_tokens_per_s_per_layer": round(w.B / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "pct_of_hbm_peak": round(100 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "kernels_us": kern,
+        "decode_only_us": round((part_us or 0) + (red_us or 0), 3),
+        "host_alloc_us_per_step": round(host_alloc_us(w), 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                     "traffic": traffic, "kernel": "paged_decode_partition",
+                     "algorithmic_bytes_per_launch": kv_bytes},
+        "kernel_hash": kernel_hash(),
+    }
+    pool.close()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+"""Lay a synthetic workload into a device pool through the library, and run
+one decode step.  Used by the GPU tests, bench.py and the smoke check.
+
+Everything here goes through the C ABI (allocator calls, kv_append,
+paged_decode); this module only moves seeded inputs to the device and keeps
+the handles.  It never imports the oracle.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+import paged_kv_cache_152_amd as pkv
+import workloads as wl
+
+APPEND_CHUNK_TOKENS = 1 << 16
+
+
+def to_device(a: np.ndarray, code: int, device="cuda"):
+    """Upload stored values (f32 / f16 / bf16 bits / E4M3 codes) as a torch tensor."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if code == wl.BF16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if code == wl.E4M3:
+        return torch.from_numpy(a).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+@dataclass
+class Prepared:
+    w: wl.Workload
+    pool: pkv.KVPool
+    seqs: list
+    q: object          # device [B][H_q][D]
+    tables: object     # device int32 [B][max_blocks]
+    lens: object       # device int32 [B]
+    step_slots: object  # device int32 [B] (the decode step's new-token slots, -1 if none)
+    k_step: object     # device [B][H_kv][D]
+    v_step: object
+    max_len: int
+    max_blocks: int
+    host_tables: np.ndarray
+    host_lens: np.ndarray
+
+    def append_step(self, stream=None):
+        self.pool.append(self.step_slots, self.k_step, self.v_step, stream)
+
+    def decode(self, out=None, workspace=None, stream=None):
+        return self.pool.decode(self.q, self.tables, self.lens, self.max_len, self.w.scale, out=out,
+                                workspace=workspace, stream=stream)
+
+    def step(self, out=None, workspace=None, stream=None):
+        """One decode step of the batch: append the new tokens, then attend."""
+        self.append_step(stream)
+        return self.decode(out, workspace, stream)
+
+
+def _append_rows(pool, slots: np.ndarray, K: np.ndarray, V: np.ndarray, src: int, device):
+    import torch
+    for s in range(0, len(slots), APPEND_CHUNK_TOKENS):
+        e = min(len(slots), s + APPEND_CHUNK_TOKENS)
+        sl = torch.from_numpy(np.ascontiguousarray(slots[s:e], np.int32)).to(device)
+        pool.append(sl, to_device(K[s:e], src, device), to_device(V[s:e], src, device))
+
+
+def poison_pool(pool: pkv.KVPool, w: wl.Workload, device="cuda"):
+    """Write NaN into every slot of the pool (through kv_append)."""
+    import torch
+    nslots = w.num_blocks * wl.BLOCK
+    src = w.src_dtype
+    tdt = pkv.torch_dtype(src) if src != wl.E4M3 else torch.bfloat16
+    for s in range(0, nslots, APPEND_CHUNK_TOKENS):
+        e = min(nslots, s + APPEND_CHUNK_TOKENS)
+        sl = torch.arange(s, e, dtype=torch.int32, device=device)
+        nan = torch.full((e - s, w.H_kv, w.D), float("nan"), dtype=tdt, device=device)
+        pool.append(sl, nan, nan)
+
+
+def prepare(w: wl.Workload, device="cuda", free_order=None, poison=False, step=0,
+            partition_tokens=0) -> Prepared:
+    """Build the pool for workload `w`, fill the prefill tokens and stage one decode step."""
+    import torch
+    order = w.free_order if free_order is None else free_order
+    pool = pkv.KVPool(w.num_blocks, w.H_kv, w.D, w.kv_dtype, free_order=order)
+    pool.set_partition(partition_tokens)
+    if w.kv_dtype == wl.E4M3:
+        pool.set_fp8_scales(*w.fp8_scales())
+    if poison:
+        poison_pool(pool, w, device)
+    seqs = [None] * w.B
+    own_slots = [None] * w.B
+    owner = min(w.sharers) if w.sharers else None
+    for op in w.build_plan():
+        if op[0] == "new":
+            _, b, n = op
+            seqs[b] = pool.seq_create()
+            own_slots[b] = (0, pool.seq_reserve(seqs[b], n))
+        elif op[0] == "fork":
+            _, b, own, p = op
+            seqs[b] = pool.seq_fork(seqs[own], p)
+        else:
+            _, b, n = op
+            own_slots[b] = (w.prefix_tokens if b in w.sharers and b != owner else 0,
+                            pool.seq_reserve(seqs[b], n))
+    step_slots = np.full(w.B, -1, np.int32)
+    kstep = np.zeros((w.B, w.H_kv, w.D), wl._NP[w.src_dtype])
+    vstep = np.zeros_like(kstep)
+    for b in range(w.B):
+        K, V = w.kv(b)
+        first, slots = own_slots[b]
+        n_pre = int(w.prefill[b])
+        if len(slots):
+            _append_rows(pool, slots, K[first:n_pre], V[first:n_pre], w.src_dtype, device)
+        if int(w.lens[b]) > n_pre:
+            step_slots[b] = pool.seq_reserve(seqs[b], 1)[0]
+            kstep[b] = K[n_pre]
+            vstep[b] = V[n_pre]
+    max_blocks = max(1, w.max_blocks_per_seq())
+    tables, lens = pool.block_tables(seqs, max_blocks)
+    assert np.array_equal(lens, w.lens), "pool lengths differ from the workload"
+    return Prepared(w=w, pool=pool, seqs=seqs, q=to_device(w.q(step), w.q_dtype, device),
+                    tables=torch.from_numpy(tables).to(device), lens=torch.from_numpy(lens).to(device),
+                    step_slots=torch.from_numpy(step_slots).to(device),
+                    k_step=to_device(kstep, w.src_dtype, device), v_step=to_device(vstep, w.src_dtype, device),
+                    max_len=w.max_len(), max_blocks=max_blocks, host_tables=tables, host_lens=lens)
+
+
+def out_to_f64(out) -> np.ndarray:
+    import torch
+    return out.detach().to(torch.float64).cpu().numpy()

@@ -1,0 +1,284 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV cache and decode
+ * attention library, libpagedkv.so.
+ *
+ * The library owns a pool of fixed-size physical KV blocks in device memory,
+ * hands them to sequences through per-sequence block tables, scatters new K/V
+ * into the pool (kv_append) and runs single-token decode attention through
+ * the tables (paged_decode).  Pages cited by address and section:
+ *   [cf1]  www.cf-1.com/news/5824798        KV memory analysis + PagedAttention
+ *   [moo]  www.mooersco.com/news/1484987    practitioner guide
+ *   [mlqm] www.mlqm.cn/news/394450          KV Cache explainer
+ *   [lqnn] m.lqnn.cn/news/219451            capacity planning and strategy
+ *   [xph]  inference.xph.ink kp-013         "KV Cache：原理与显存占比"
+ *
+ * Conventions for every entry point
+ *   - Every function returns a pkv_status (0 = PKV_OK) unless stated, and
+ *     never lets a C++ exception cross the ABI.  On failure
+ *     pkv_last_error() returns a thread-local message.
+ *   - "host" pointers are CPU memory, "device" pointers are HIP device memory
+ *     of the GPU current when the pool was created.  The caller owns every
+ *     pointer it passes; the library copies what it keeps.
+ *   - Streams are hipStream_t handles passed as void*; NULL is the default
+ *     stream.  kv_append and paged_decode are asynchronous on that stream:
+ *     inputs must stay alive and unmodified until the stream has passed them.
+ *   - A pool is not thread-safe: calls on one pool must be serialised by the
+ *     caller.
+ *   - Arguments are validated before any device work.  Device-side contents
+ *     (slot values, table entries, context lengths) cannot be validated on the
+ *     host; the kernels bound-check them instead and skip what is out of
+ *     range (documented per call), so no input can make a kernel read or
+ *     write outside the pool or the caller's buffers.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned, bad combination */
+    PKV_ERR_NO_BLOCKS = 2,     /* pool exhausted; nothing was changed */
+    PKV_ERR_OUT_OF_RANGE = 3,  /* a table would not fit the caller's width, length overflow */
+    PKV_ERR_STATE = 4,         /* unknown or freed sequence, wrong pool kind for the call */
+    PKV_ERR_UNSUPPORTED = 5,   /* a (dtype, head_dim, group) combination with no kernel */
+    PKV_ERR_DEVICE = 6         /* a HIP runtime call failed (allocation, copy, launch) */
+} pkv_status;
+
+/* Storage / element types. */
+typedef enum {
+    PKV_F32 = 0,
+    PKV_F16 = 1,
+    PKV_BF16 = 2,
+    PKV_FP8_E4M3 = 3           /* OCP 8-bit float E4M3 ("FN": max 448, NaN 0x7F/0xFF) */
+} pkv_dtype;
+
+typedef struct kv_pool kv_pool_t;
+
+typedef struct {
+    void* k_pool;              /* device; [num_blocks][kv_heads][block_size][head_dim] */
+    void* v_pool;              /* device; same layout, separate buffer */
+    float* k_scale;            /* device; [kv_heads] (FP8 pools only, else NULL) */
+    float* v_scale;            /* device; [kv_heads] (FP8 pools only, else NULL) */
+    uint64_t pool_bytes;       /* bytes of ONE of k_pool / v_pool */
+    uint64_t block_bytes;      /* bytes of one (block, kv head) tile = block_size*head_dim*elem */
+    uint64_t total_bytes;      /* device bytes owned: 2*pool_bytes + scales */
+    int32_t num_blocks, block_size, kv_heads, head_dim, dtype, elem_bytes;
+    int32_t free_blocks;       /* refcount 0 */
+    int32_t used_blocks;       /* refcount >= 1 */
+    int32_t shared_blocks;     /* refcount >= 2 */
+    int32_t live_seqs;
+    int32_t host_only;         /* 1: metadata-only pool, no device memory */
+    int32_t partition_tokens;  /* current paged_decode partition setting (0 = automatic) */
+} kv_pool_info_t;
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* KV size formula, [cf1] §1.2 and [xph] "公式与模型": bytes of K and V for
+ * `tokens` cached tokens of each of `seqs` sequences:
+ *   2 * layers * kv_heads * head_dim * elem_bytes * tokens * seqs.
+ * Returns 0 on invalid input (any of the first four <= 0, tokens or seqs < 0),
+ * as the budget script of [lqnn] §2 refuses such shapes. */
+uint64_t kv_cache_bytes(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                        int32_t elem_bytes, int64_t tokens, int64_t seqs);
+
+/* ---------------------------------------------------------------------------
+ * Pool
+ * ------------------------------------------------------------------------ */
+
+/* Create a pool: pre-allocate the K and V block pools once ([moo] §2.2
+ * "pre-allocation"; [cf1] §3.1 "one unified pool of fixed-size blocks"), with
+ * the per-block layout [moo] §3.1 gives for one layer and separate K and V
+ * buffers: [num_blocks][kv_heads][block_size][head_dim], 256-byte aligned,
+ * zero-filled.  FP8 pools also hold per-KV-head fp32 scales for K and V
+ * ([lqnn] §4, per-attention-head scales), initialised to 1.
+ *   block_size        must be 16 ([cf1] §3.1 default).
+ *   head_dim          16, 64 or 128 (a 16-token tile must be >= 256 bytes).
+ *   dtype             a pkv_dtype.
+ *   initial_free_order host, nullable: a permutation of 0..num_blocks-1 giving
+ *                     the initial order of the FIFO free list; NULL means
+ *                     0, 1, ..., num_blocks-1.
+ * Errors: INVALID_ARG (<= 0 sizes, not a permutation, null out),
+ * UNSUPPORTED (block_size != 16, head_dim, dtype), DEVICE (allocation). */
+int kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t kv_heads,
+                   int32_t head_dim, int32_t dtype, const int32_t* initial_free_order,
+                   kv_pool_t** out);
+
+/* Same pool bookkeeping with no device memory: block tables, refcounts and
+ * slot mappings only (capacity planning, host tests).  kv_append,
+ * paged_decode and kv_pool_copy_to_host on it return PKV_ERR_STATE after
+ * their argument checks.  Touches no HIP API. */
+int kv_pool_create_host_only(int32_t num_blocks, int32_t block_size, int32_t kv_heads,
+                             int32_t head_dim, int32_t dtype,
+                             const int32_t* initial_free_order, kv_pool_t** out);
+
+/* Free the pool, its device memory and every sequence.  NULL is a no-op.  The
+ * caller must make sure no stream still uses the pool. */
+int kv_pool_destroy(kv_pool_t* pool);
+
+/* Describe the pool (pointers, sizes, layout, block counts). */
+int kv_pool_info(const kv_pool_t* pool, kv_pool_info_t* out);
+
+/* Set the static per-KV-head FP8 scales (host arrays of kv_heads floats).
+ * Stored values are code = E4M3_rne_satfinite(x * (1/scale)) and read back as
+ * decode(code) * scale ([lqnn] §4: the scale sets the dynamic range; outliers
+ * beyond it saturate).  The library keeps inv = 1.0f/scale (one fp32
+ * division) for kv_append.  Synchronous.
+ * Errors: STATE (not an FP8 pool), INVALID_ARG (null, <= 0 or non-finite). */
+int kv_pool_set_fp8_scales(kv_pool_t* pool, const float* k_scale, const float* v_scale);
+
+/* ---------------------------------------------------------------------------
+ * Sequences and block tables (host only; [cf1] §3.2-§3.3)
+ *
+ * Free list: FIFO, seeded by initial_free_order.  A sequence takes blocks
+ * from the front when a new token position p has p % block_size == 0 (only
+ * its last block is ever partly filled).  Releasing a sequence decrements the
+ * refcount of each of its blocks in logical order; blocks reaching 0 go to the
+ * back of the free list.  Slot of logical position p:
+ *   table[p / block_size] * block_size + p % block_size.
+ * ------------------------------------------------------------------------ */
+
+/* New sequence with an empty table; ids are never reused. */
+int kv_seq_create(kv_pool_t* pool, int32_t* seq_id);
+
+/* Reserve n_tokens new positions at the end of `seq`, taking blocks on
+ * demand, and write their slots to slot_mapping_out (host, n_tokens int32;
+ * may be NULL when n_tokens == 0).  All or nothing: on NO_BLOCKS nothing
+ * changed.  Errors: STATE (unknown seq), INVALID_ARG (n_tokens < 0),
+ * NO_BLOCKS, OUT_OF_RANGE (length beyond INT32_MAX). */
+int kv_seq_reserve(kv_pool_t* pool, int32_t seq, int32_t n_tokens, int32_t* slot_mapping_out);
+
+/* New sequence sharing the first n_shared_tokens of `parent` by reference:
+ * the child's table points at the same n_shared/block_size physical blocks,
+ * each of whose refcount is incremented ([cf1] §3.3 shared prefix; [lqnn] §3
+ * "prefixes shared by reference").  n_shared_tokens must be a multiple of
+ * block_size and <= the parent's length (whole blocks only; a shared block is
+ * never written, so no copy is ever needed).  Errors: STATE, INVALID_ARG. */
+int kv_seq_fork(kv_pool_t* pool, int32_t parent, int32_t n_shared_tokens, int32_t* child);
+
+/* Release a sequence (see above).  Errors: STATE (unknown or already freed). */
+int kv_seq_free(kv_pool_t* pool, int32_t seq);
+
+/* Current length (tokens) of a sequence.  Errors: STATE. */
+int kv_seq_length(const kv_pool_t* pool, int32_t seq, int32_t* len);
+
+/* Block tables and context lengths of n sequences, for upload by the caller:
+ * tables_out (host, [n][max_blocks_per_seq] int32; unused entries -1) and
+ * context_lens_out (host, [n] int32).  Errors: STATE (unknown seq),
+ * OUT_OF_RANGE (a table wider than max_blocks_per_seq), INVALID_ARG. */
+int kv_block_tables(const kv_pool_t* pool, const int32_t* seqs, int32_t n,
+                    int32_t max_blocks_per_seq, int32_t* tables_out,
+                    int32_t* context_lens_out);
+
+/* Refcount of a physical block (inspection).  Errors: INVALID_ARG. */
+int kv_block_refcount(const kv_pool_t* pool, int32_t block, int32_t* out);
+
+/* Copy the free list, front first, into out (host, capacity cap);
+ * *n receives its length.  Errors: OUT_OF_RANGE if cap is too small. */
+int kv_free_list(const kv_pool_t* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* ---------------------------------------------------------------------------
+ * Device work
+ * ------------------------------------------------------------------------ */
+
+/* Scatter new keys and values into the pool ([cf1] §1.1 and [mlqm] 四: only
+ * the new token's K/V are computed and appended).  For token t and KV head g,
+ *   pool[slot / bs][g][slot % bs][:] = k_new[t][g][:]   (same for V)
+ * where slot = slot_mapping[t].
+ *   slot_mapping  device, [T] int32.  A slot < 0 or >= num_blocks*block_size
+ *                 skips that token.  Duplicate slots race (undefined which
+ *                 token wins).
+ *   k_new, v_new  device, [T][kv_heads][head_dim] of src_dtype, 16-byte
+ *                 aligned.  src_dtype must equal the pool dtype, or be BF16
+ *                 or F32 for an FP8 pool, which quantises in the kernel:
+ *                 code = E4M3_rne_satfinite(x * inv_scale[g]), NaN -> 0x7F.
+ * T == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED (dtype pairing),
+ * STATE (host-only pool), DEVICE (launch). */
+int kv_append(kv_pool_t* pool, const int32_t* slot_mapping, int32_t T,
+              const void* k_new, const void* v_new, int32_t src_dtype, void* stream);
+
+/* Single-token decode attention through block tables ([mlqm] 二 and 四:
+ * softmax(Q K^T * scale) V for the newest query over every cached token;
+ * [cf1] §3.1 block table; [mlqm] 六 GQA).  For sequence b, query head h,
+ * G = H_q / kv_heads, g = h / G, n = context_lens[b]:
+ *   z_j = scale * <q[b][h], K_b[j][g]>,   j = 0..n-1 (logical order; the
+ *         newest token, appended before the call, is j = n-1)
+ *   out[b][h] = sum_j softmax(z)_j * V_b[j][g]
+ * where K_b[j] lives in block block_tables[b][j / 16], row j % 16.  For an FP8
+ * pool the stored values are decode(code) * k_scale[g] (resp. v_scale[g]).
+ *   q             device [B][H_q][head_dim] of q_dtype (= pool dtype; BF16
+ *                 for an FP8 pool), 16-byte aligned.
+ *   block_tables  device [B][max_blocks_per_seq] int32.  Entries outside
+ *                 [0, num_blocks) make their 16 tokens count as absent.
+ *   context_lens  device [B] int32, each clamped to
+ *                 [0, min(max_context_len, 16*max_blocks_per_seq)]; rows with
+ *                 length 0 get out = 0.
+ *   max_context_len host upper bound of context_lens (sizes the grid).
+ *   out           device [B][H_q][head_dim] of q_dtype, 16-byte aligned.
+ *   workspace     device scratch of at least paged_decode_workspace_bytes()
+ *                 for these B, H_q, max_context_len (NULL allowed if 0).
+ * Work is split into partitions of the context; each partition keeps a running
+ * max and sum (online softmax) and a second kernel merges partitions.
+ * Errors: INVALID_ARG, UNSUPPORTED (no kernel for dtype/head_dim/group: the
+ * library refuses rather than fall back), STATE (host-only pool), DEVICE. */
+int paged_decode(kv_pool_t* pool, const void* q, int32_t q_dtype, int32_t B, int32_t H_q,
+                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, int32_t max_context_len, float scale,
+                 void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes paged_decode needs for these sizes with the pool's current
+ * partition setting (0 if one partition covers max_context_len). */
+size_t paged_decode_workspace_bytes(const kv_pool_t* pool, int32_t B, int32_t H_q,
+                                    int32_t max_context_len);
+
+/* Partition size (tokens) paged_decode uses: 0 = automatic, else a multiple
+ * of 64 in [64, 1048576].  Affects only rounding order, never the result
+ * beyond floating-point reassociation.  Errors: INVALID_ARG. */
+int paged_decode_set_partition(kv_pool_t* pool, int32_t partition_tokens);
+
+/* Partition size paged_decode would use for these sizes (resolves 0). */
+int32_t paged_decode_partition_tokens(const kv_pool_t* pool, int32_t B, int32_t H_q,
+                                      int32_t max_context_len);
+
+/* Synchronous copy of the whole K and V pools to host buffers of pool_bytes
+ * each (inspection and tests).  Either pointer may be NULL.
+ * Errors: STATE (host-only pool), DEVICE. */
+int kv_pool_copy_to_host(const kv_pool_t* pool, void* k_dst, void* v_dst);
+
+/* ---------------------------------------------------------------------------
+ * Measurement
+ * ------------------------------------------------------------------------ */
+
+/* Per-kernel timing: while enabled, every kernel the pool launches is
+ * bracketed by HIP events on its launch stream.  pkv_profile_read waits for
+ * the recorded events, fills up to cap entries of `out` with the launches
+ * and summed device milliseconds per kernel name since the last read, and
+ * resets the counters.  At most 65536 launches per kernel are kept between
+ * reads; more are counted in `dropped`. */
+typedef struct {
+    char name[48];
+    int64_t launches;
+    int64_t dropped;
+    double total_ms;
+} pkv_kernel_stat_t;
+
+int pkv_profile_enable(kv_pool_t* pool, int32_t on);
+int pkv_profile_read(kv_pool_t* pool, pkv_kernel_stat_t* out, int32_t cap, int32_t* n);
+
+/* Plain device-to-device copy of `bytes` (a multiple of 16, both pointers
+ * 16-byte aligned) with 16-byte loads and stores: the reference kernel
+ * against which HBM traffic counters are scaled.  Asynchronous on stream.
+ * Errors: INVALID_ARG, DEVICE. */
+int pkv_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

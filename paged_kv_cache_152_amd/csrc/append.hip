@@ -1,0 +1,160 @@
+// kv_append: scatter the new tokens' K and V into their pool slots, and the
+// plain copy kernel used to calibrate HBM traffic counters.
+//
+// Only the new token's K/V are computed each decode step and appended to the
+// cache (www.cf-1.com/news/5824798 §1.1; www.mlqm.cn/news/394450 section 四);
+// with a pre-allocated pool the append is a store at an index
+// (www.mooersco.com/news/1484987 §2.2).  Slot s addresses block s / 16,
+// row s % 16 of the [num_blocks][H_kv][16][D] pool.
+//
+// One thread moves one 16-byte chunk of a destination row.  For an FP8 pool
+// the source (bf16 or fp32) is multiplied by the per-head inverse scale in
+// fp32 and rounded to OCP E4M3 (nearest, ties to even, saturating at 448,
+// NaN -> 0x7F), the storage convention of m.lqnn.cn/news/219451 §4.
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+// fp32 -> OCP E4M3 ("FN": bias 7, no infinities, S.1111.111 = NaN, max 448),
+// round to nearest, ties to even, values beyond 448 saturate.  Integer-only.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0x7Fu;                 // NaN
+    if (a >= 0x43E00000u) return sign | 0x7Eu;         // |x| >= 448 (incl. inf): saturate
+    const uint32_t e32 = a >> 23;                      // biased fp32 exponent
+    if (e32 >= 121u) {                                 // |x| >= 2^-6: E4M3 normal range
+        const uint32_t man = a & 0x7FFFFFu;
+        uint32_t code = ((e32 - 120u) << 3) | (man >> 20);
+        const uint32_t rem = man & 0xFFFFFu;
+        if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ++code;  // carries into exponent
+        return sign | code;                            // code <= 0x7E since |x| < 448
+    }
+    // Subnormal E4M3: value = k * 2^-9, k = round(|x| * 2^9).
+    // |x| = sig * 2^(e - 150) with sig the 24-bit significand (e >= 1) or the raw
+    // fraction (e == 0, where the exponent is that of e == 1).
+    const uint32_t sig = e32 ? ((a & 0x7FFFFFu) | 0x800000u) : (a & 0x7FFFFFu);
+    const uint32_t shift = 141u - (e32 ? e32 : 1u);    // >= 21
+    if (shift >= 25u) return sign;                     // |x| < 2^-10: rounds to zero
+    uint32_t k = sig >> shift;
+    const uint32_t rem = sig & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1u);
+    if (rem > half || (rem == half && (k & 1u))) ++k;  // k == 8 is the smallest normal
+    return sign | k;
+}
+
+template <int SRC>
+__device__ __forceinline__ float src_elem(const char* p, int i) {
+    if constexpr (SRC == DT_F32) return reinterpret_cast<const float*>(p)[i];
+    else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);  // bf16
+}
+
+// Same-dtype append: one 16-byte chunk per thread.
+__global__ __launch_bounds__(256) void kv_append_copy(AppendParams p, int row_bytes) {
+    const int chunks = row_bytes / 16;
+    const int64_t per_kv = (int64_t)p.T * p.H_kv * chunks;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= 2 * per_kv) return;
+    const int which = idx >= per_kv;                   // 0: K, 1: V
+    int64_t rem = idx - which * per_kv;
+    const int chunk = (int)(rem % chunks);
+    rem /= chunks;
+    const int g = (int)(rem % p.H_kv);
+    const int t = (int)(rem / p.H_kv);
+    const int32_t slot = p.slots[t];
+    if (slot < 0 || (int64_t)slot >= p.num_slots) return;
+    const int64_t blk = slot / kBlock, row = slot % kBlock;
+    const char* src = reinterpret_cast<const char*>(which ? p.v_src : p.k_src) +
+                      ((int64_t)t * p.H_kv + g) * row_bytes + (int64_t)chunk * 16;
+    char* dst = reinterpret_cast<char*>(which ? p.v_pool : p.k_pool) +
+                ((blk * p.H_kv + g) * kBlock + row) * row_bytes + (int64_t)chunk * 16;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+
+// Quantising append into an FP8 pool: 16 codes (one 16-byte chunk) per thread.
+template <int SRC>
+__global__ __launch_bounds__(256) void kv_append_fp8(AppendParams p) {
+    constexpr int SE = SRC == DT_F32 ? 4 : 2;
+    const int chunks = p.D / 16;
+    const int64_t per_kv = (int64_t)p.T * p.H_kv * chunks;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= 2 * per_kv) return;
+    const int which = idx >= per_kv;
+    int64_t rem = idx - which * per_kv;
+    const int chunk = (int)(rem % chunks);
+    rem /= chunks;
+    const int g = (int)(rem % p.H_kv);
+    const int t = (int)(rem / p.H_kv);
+    const int32_t slot = p.slots[t];
+    if (slot < 0 || (int64_t)slot >= p.num_slots) return;
+    const int64_t blk = slot / kBlock, row = slot % kBlock;
+    const float inv = (which ? p.v_inv : p.k_inv)[g];
+    const char* src = reinterpret_cast<const char*>(which ? p.v_src : p.k_src) +
+                      (((int64_t)t * p.H_kv + g) * p.D + (int64_t)chunk * 16) * SE;
+    uint32_t words[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) packed |= e4m3_from_f32(src_elem<SRC>(src, 4 * w + k) * inv) << (8 * k);
+        words[w] = packed;
+    }
+    char* dst = reinterpret_cast<char*>(which ? p.v_pool : p.k_pool) +
+                ((blk * p.H_kv + g) * kBlock + row) * p.D + (int64_t)chunk * 16;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+}
+
+// Plain copy, 16 bytes per load/store, four independent chunks per thread per step.
+__global__ __launch_bounds__(256) void pkv_copy_kernel(uint4* __restrict__ dst,
+                                                       const uint4* __restrict__ src, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        dst[i] = a;
+        dst[i + stride] = b;
+        dst[i + 2 * stride] = c;
+        dst[i + 3 * stride] = d;
+    }
+    for (; i < n; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream) {
+    if (p.T <= 0) return hipSuccess;
+    AppendParams arg = p;
+    if (p.dst_dt == p.src_dt) {
+        int row_bytes = p.D * elem_bytes(p.dst_dt);
+        const int64_t threads = 2LL * p.T * p.H_kv * (row_bytes / 16);
+        const unsigned blocks = (unsigned)((threads + 255) / 256);
+        void* args[] = {&arg, &row_bytes};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kv_append_copy), dim3(blocks), dim3(256), args,
+                               0, stream);
+    }
+    if (p.dst_dt == DT_FP8 && (p.src_dt == DT_BF16 || p.src_dt == DT_F32)) {
+        const int64_t threads = 2LL * p.T * p.H_kv * (p.D / 16);
+        const unsigned blocks = (unsigned)((threads + 255) / 256);
+        void* args[] = {&arg};
+        const void* fn = p.src_dt == DT_BF16 ? reinterpret_cast<const void*>(kv_append_fp8<DT_BF16>)
+                                             : reinterpret_cast<const void*>(kv_append_fp8<DT_F32>);
+        return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    int64_t n = (int64_t)(bytes / 16);
+    if (n == 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;          // grid-stride beyond 64 workgroups per CU
+    uint4* d = reinterpret_cast<uint4*>(dst);
+    const uint4* s = reinterpret_cast<const uint4*>(src);
+    void* args[] = {&d, &s, &n};
+    return hipLaunchKernel(reinterpret_cast<const void*>(pkv_copy_kernel), dim3((unsigned)blocks), dim3(256),
+                           args, 0, stream);
+}
+
+}  // namespace pkv

@@ -1,0 +1,58 @@
+// Internal interface between the host core (pool.cpp) and the HIP kernels.
+// Not part of the public ABI (include/pagedkv.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlock = 16;        // tokens per physical block
+constexpr int kDecodeWaves = 4;   // waves per decode workgroup
+constexpr int kMaxGroupPerWg = 8; // query heads one decode workgroup serves
+
+enum Dt : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+
+inline int elem_bytes(int32_t dt) { return dt == DT_F32 ? 4 : (dt == DT_FP8 ? 1 : 2); }
+
+struct AppendParams {
+    const int32_t* slots;
+    const void* k_src;
+    const void* v_src;
+    void* k_pool;
+    void* v_pool;
+    const float* k_inv;   // FP8 pools: per-head 1/scale
+    const float* v_inv;
+    int64_t num_slots;    // num_blocks * kBlock
+    int32_t T, H_kv, D;
+    int32_t src_dt, dst_dt;
+};
+
+struct DecodeParams {
+    const void* k_pool;
+    const void* v_pool;
+    const float* k_scale;     // FP8 pools only
+    const float* v_scale;
+    const void* q;            // [B][H_q][D]
+    void* out;                // [B][H_q][D]
+    const int32_t* tables;    // [B][max_blocks]
+    const int32_t* lens;      // [B]
+    float* ws_ml;             // [B][H_q][max_parts][2]  (running max, sum) per partition
+    float* ws_o;              // [B][H_q][max_parts][D]  unnormalised partial output
+    int32_t B, H_q, H_kv, G, D, num_blocks, max_blocks, max_len;
+    int32_t part_tokens, max_parts;
+    int32_t kv_dt, q_dt;
+    float scale;              // softmax scale as given
+};
+
+// Launch one kernel each; return hipSuccess or the launch error.
+// Unsupported combinations are filtered on the host before these are called.
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
+bool decode_supported(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G);
+int decode_heads_per_wg(int32_t G);
+hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace pkv

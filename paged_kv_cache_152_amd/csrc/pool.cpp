@@ -1,0 +1,644 @@
+// Host core of libpagedkv: the block pool, its allocator, argument checks and
+// the C ABI declared in include/pagedkv.h.
+//
+// Allocator (www.cf-1.com/news/5824798 §3.1-§3.3; m.lqnn.cn/news/219451 §3):
+// one pool of fixed 16-token blocks, a FIFO free list seeded by the caller, a
+// per-sequence block table grown on demand (a block is taken only when a new
+// position starts one, so only the last block is ever partly filled), and a
+// per-block reference count so several tables can share prefix blocks.  A
+// block whose count drops to zero goes to the back of the free list.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <limits>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+// The library is built with hidden visibility; only the C ABI is exported.
+#pragma GCC visibility push(default)
+#include "../../include/pagedkv.h"
+#pragma GCC visibility pop
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return PKV_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PKV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Seq {
+    std::vector<int32_t> blocks;
+    int32_t len = 0;
+};
+
+constexpr int kMaxTimed = 65536;
+
+struct KernelTimer {
+    std::string name;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+    int64_t launches = 0, dropped = 0;
+};
+
+}  // namespace
+
+struct kv_pool {
+    int32_t num_blocks = 0, block_size = 0, kv_heads = 0, head_dim = 0, dtype = 0, elem = 0;
+    bool host_only = true;
+    int device = 0;
+    void* k_pool = nullptr;
+    void* v_pool = nullptr;
+    float* scales = nullptr;   // device: k_scale[H], v_scale[H], k_inv[H], v_inv[H]
+    uint64_t pool_bytes = 0, block_bytes = 0;
+    int32_t partition_tokens = 0;
+
+    std::deque<int32_t> free_list;
+    std::vector<int32_t> ref;
+    std::unordered_map<int32_t, Seq> seqs;
+    int32_t next_id = 0;
+    int32_t shared = 0;        // blocks with refcount >= 2
+
+    bool profiling = false;
+    std::vector<KernelTimer> timers;
+    std::vector<hipEvent_t> spare_events;
+};
+
+namespace {
+
+bool dtype_known(int32_t dt) { return dt >= PKV_F32 && dt <= PKV_FP8_E4M3; }
+
+int elem_of(int32_t dt) { return pkv::elem_bytes(dt); }
+
+void ref_inc(kv_pool* p, int32_t b) {
+    if (++p->ref[b] == 2) ++p->shared;
+}
+
+void ref_dec(kv_pool* p, int32_t b) {
+    if (p->ref[b]-- == 2) --p->shared;
+}
+
+int create_common(int32_t num_blocks, int32_t block_size, int32_t kv_heads, int32_t head_dim,
+                  int32_t dtype, const int32_t* order, kv_pool_t** out, bool host_only) {
+    if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (num_blocks <= 0 || block_size <= 0 || kv_heads <= 0 || head_dim <= 0)
+        return fail(PKV_ERR_INVALID_ARG, "sizes must be > 0 (num_blocks %d, block_size %d, kv_heads %d, head_dim %d)",
+                    num_blocks, block_size, kv_heads, head_dim);
+    if (!dtype_known(dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (block_size != pkv::kBlock) return fail(PKV_ERR_UNSUPPORTED, "block_size must be 16, got %d", block_size);
+    if (head_dim != 16 && head_dim != 64 && head_dim != 128)
+        return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 16, 64 or 128, got %d", head_dim);
+    if ((int64_t)num_blocks * block_size > std::numeric_limits<int32_t>::max())
+        return fail(PKV_ERR_INVALID_ARG, "num_blocks * block_size must fit int32 slots");
+    if (kv_heads > 65535) return fail(PKV_ERR_INVALID_ARG, "kv_heads too large");
+    std::vector<int32_t> ord(num_blocks);
+    if (order) {
+        std::vector<char> seen(num_blocks, 0);
+        for (int32_t i = 0; i < num_blocks; ++i) {
+            const int32_t b = order[i];
+            if (b < 0 || b >= num_blocks || seen[b])
+                return fail(PKV_ERR_INVALID_ARG, "initial_free_order is not a permutation of 0..%d", num_blocks - 1);
+            seen[b] = 1;
+            ord[i] = b;
+        }
+    } else {
+        for (int32_t i = 0; i < num_blocks; ++i) ord[i] = i;
+    }
+    kv_pool* p = new (std::nothrow) kv_pool();
+    if (!p) return fail(PKV_ERR_DEVICE, "host allocation failed");
+    p->num_blocks = num_blocks;
+    p->block_size = block_size;
+    p->kv_heads = kv_heads;
+    p->head_dim = head_dim;
+    p->dtype = dtype;
+    p->elem = elem_of(dtype);
+    p->host_only = host_only;
+    p->block_bytes = (uint64_t)block_size * head_dim * p->elem;
+    p->pool_bytes = (uint64_t)num_blocks * kv_heads * p->block_bytes;
+    p->free_list.assign(ord.begin(), ord.end());
+    p->ref.assign(num_blocks, 0);
+    if (!host_only) {
+        hipError_t e = hipGetDevice(&p->device);
+        if (e == hipSuccess) e = hipMalloc(&p->k_pool, p->pool_bytes);
+        if (e == hipSuccess) e = hipMalloc(&p->v_pool, p->pool_bytes);
+        if (e == hipSuccess) e = hipMemset(p->k_pool, 0, p->pool_bytes);
+        if (e == hipSuccess) e = hipMemset(p->v_pool, 0, p->pool_bytes);
+        if (e == hipSuccess && dtype == PKV_FP8_E4M3) {
+            e = hipMalloc(&p->scales, sizeof(float) * 4 * kv_heads);
+            if (e == hipSuccess) {
+                std::vector<float> ones(4 * kv_heads, 1.0f);
+                e = hipMemcpy(p->scales, ones.data(), sizeof(float) * 4 * kv_heads, hipMemcpyHostToDevice);
+            }
+        }
+        if (e != hipSuccess) {
+            int rc = hip_fail(e, "pool device allocation");
+            kv_pool_destroy(p);
+            return rc;
+        }
+    }
+    *out = p;
+    return ok();
+}
+
+Seq* find_seq(kv_pool* p, int32_t id) {
+    auto it = p->seqs.find(id);
+    return it == p->seqs.end() ? nullptr : &it->second;
+}
+
+const Seq* find_seq(const kv_pool* p, int32_t id) {
+    auto it = p->seqs.find(id);
+    return it == p->seqs.end() ? nullptr : &it->second;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// ---------------------------------------------------------------- profiling
+hipEvent_t take_event(kv_pool* p) {
+    if (!p->spare_events.empty()) {
+        hipEvent_t e = p->spare_events.back();
+        p->spare_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+KernelTimer& timer_for(kv_pool* p, const char* name) {
+    for (auto& t : p->timers)
+        if (t.name == name) return t;
+    p->timers.push_back(KernelTimer{name, {}, 0, 0});
+    return p->timers.back();
+}
+
+// Launch `fn` on `stream`, bracketed by events when profiling.
+template <class F>
+hipError_t timed_launch(kv_pool* p, const char* name, hipStream_t stream, F&& fn) {
+    if (!p->profiling) return fn();
+    KernelTimer& t = timer_for(p, name);
+    ++t.launches;
+    if ((int)t.pending.size() >= kMaxTimed) {
+        ++t.dropped;
+        return fn();
+    }
+    hipEvent_t a = take_event(p), b = take_event(p);
+    if (!a || !b) {
+        ++t.dropped;
+        if (a) p->spare_events.push_back(a);
+        if (b) p->spare_events.push_back(b);
+        return fn();
+    }
+    hipEventRecord(a, stream);
+    hipError_t e = fn();
+    hipEventRecord(b, stream);
+    t.pending.emplace_back(a, b);
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t kv_cache_bytes(int32_t layers, int32_t kv_heads, int32_t head_dim, int32_t elem_bytes,
+                        int64_t tokens, int64_t seqs) {
+    if (layers <= 0 || kv_heads <= 0 || head_dim <= 0 || elem_bytes <= 0 || tokens < 0 || seqs < 0) return 0;
+    return 2ull * (uint64_t)layers * (uint64_t)kv_heads * (uint64_t)head_dim * (uint64_t)elem_bytes *
+           (uint64_t)tokens * (uint64_t)seqs;
+}
+
+int kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                   const int32_t* initial_free_order, kv_pool_t** out) {
+    try {
+        return create_common(num_blocks, block_size, kv_heads, head_dim, dtype, initial_free_order, out, false);
+    } catch (...) {
+        return fail(PKV_ERR_DEVICE, "kv_pool_create: host exception");
+    }
+}
+
+int kv_pool_create_host_only(int32_t num_blocks, int32_t block_size, int32_t kv_heads, int32_t head_dim,
+                             int32_t dtype, const int32_t* initial_free_order, kv_pool_t** out) {
+    try {
+        return create_common(num_blocks, block_size, kv_heads, head_dim, dtype, initial_free_order, out, true);
+    } catch (...) {
+        return fail(PKV_ERR_DEVICE, "kv_pool_create_host_only: host exception");
+    }
+}
+
+int kv_pool_destroy(kv_pool_t* pool) {
+    if (!pool) return ok();
+    if (!pool->host_only) {
+        for (auto& t : pool->timers)
+            for (auto& ev : t.pending) {
+                hipEventDestroy(ev.first);
+                hipEventDestroy(ev.second);
+            }
+        for (hipEvent_t e : pool->spare_events) hipEventDestroy(e);
+        if (pool->k_pool) hipFree(pool->k_pool);
+        if (pool->v_pool) hipFree(pool->v_pool);
+        if (pool->scales) hipFree(pool->scales);
+    }
+    delete pool;
+    return ok();
+}
+
+int kv_pool_info(const kv_pool_t* p, kv_pool_info_t* out) {
+    if (!p || !out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    std::memset(out, 0, sizeof *out);
+    out->k_pool = p->k_pool;
+    out->v_pool = p->v_pool;
+    out->k_scale = p->scales;
+    out->v_scale = p->scales ? p->scales + p->kv_heads : nullptr;
+    out->pool_bytes = p->pool_bytes;
+    out->block_bytes = p->block_bytes;
+    out->total_bytes = p->host_only ? 0 : 2 * p->pool_bytes + (p->scales ? 4ull * sizeof(float) * p->kv_heads : 0);
+    out->num_blocks = p->num_blocks;
+    out->block_size = p->block_size;
+    out->kv_heads = p->kv_heads;
+    out->head_dim = p->head_dim;
+    out->dtype = p->dtype;
+    out->elem_bytes = p->elem;
+    out->free_blocks = (int32_t)p->free_list.size();
+    out->used_blocks = p->num_blocks - out->free_blocks;
+    out->shared_blocks = p->shared;
+    out->live_seqs = (int32_t)p->seqs.size();
+    out->host_only = p->host_only ? 1 : 0;
+    out->partition_tokens = p->partition_tokens;
+    return ok();
+}
+
+int kv_pool_set_fp8_scales(kv_pool_t* p, const float* k_scale, const float* v_scale) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    if (p->dtype != PKV_FP8_E4M3) return fail(PKV_ERR_STATE, "scales apply to FP8 pools only");
+    if (!k_scale || !v_scale) return fail(PKV_ERR_INVALID_ARG, "NULL scale array");
+    const int H = p->kv_heads;
+    std::vector<float> h(4 * H);
+    for (int i = 0; i < H; ++i) {
+        if (!(k_scale[i] > 0.0f) || !std::isfinite(k_scale[i]) || !(v_scale[i] > 0.0f) || !std::isfinite(v_scale[i]))
+            return fail(PKV_ERR_INVALID_ARG, "scales must be finite and > 0 (head %d)", i);
+        h[i] = k_scale[i];
+        h[H + i] = v_scale[i];
+        h[2 * H + i] = 1.0f / k_scale[i];
+        h[3 * H + i] = 1.0f / v_scale[i];
+    }
+    if (p->host_only) return ok();
+    hipError_t e = hipMemcpy(p->scales, h.data(), sizeof(float) * 4 * H, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "scale upload");
+    return ok();
+}
+
+// ------------------------------------------------------------------ sequences
+int kv_seq_create(kv_pool_t* p, int32_t* seq_id) {
+    if (!p || !seq_id) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    if (p->next_id == std::numeric_limits<int32_t>::max()) return fail(PKV_ERR_OUT_OF_RANGE, "sequence ids exhausted");
+    try {
+        const int32_t id = p->next_id++;
+        p->seqs.emplace(id, Seq{});
+        *seq_id = id;
+    } catch (...) {
+        return fail(PKV_ERR_DEVICE, "host allocation failed");
+    }
+    return ok();
+}
+
+int kv_seq_reserve(kv_pool_t* p, int32_t seq, int32_t n_tokens, int32_t* slots) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    Seq* s = find_seq(p, seq);
+    if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
+    if (n_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "n_tokens < 0");
+    if (n_tokens > 0 && !slots) return fail(PKV_ERR_INVALID_ARG, "slot_mapping_out is NULL");
+    const int64_t new_len = (int64_t)s->len + n_tokens;
+    if (new_len > std::numeric_limits<int32_t>::max()) return fail(PKV_ERR_OUT_OF_RANGE, "sequence length overflow");
+    const int bs = p->block_size;
+    const int64_t need = (new_len + bs - 1) / bs - (int64_t)s->blocks.size();
+    if (need > (int64_t)p->free_list.size())
+        return fail(PKV_ERR_NO_BLOCKS, "need %lld blocks, %zu free", (long long)need, p->free_list.size());
+    if (n_tokens > 0 && s->len % bs != 0 && p->ref[s->blocks.back()] != 1)
+        return fail(PKV_ERR_STATE, "would write into a shared block");
+    try {
+        s->blocks.reserve(s->blocks.size() + (size_t)need);
+    } catch (...) {
+        return fail(PKV_ERR_DEVICE, "host allocation failed");
+    }
+    for (int64_t i = 0; i < need; ++i) {
+        const int32_t b = p->free_list.front();
+        p->free_list.pop_front();
+        p->ref[b] = 1;
+        s->blocks.push_back(b);
+    }
+    for (int64_t pos = s->len, i = 0; pos < new_len; ++pos, ++i)
+        slots[i] = s->blocks[pos / bs] * bs + (int32_t)(pos % bs);
+    s->len = (int32_t)new_len;
+    return ok();
+}
+
+int kv_seq_fork(kv_pool_t* p, int32_t parent, int32_t n_shared, int32_t* child) {
+    if (!p || !child) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    Seq* s = find_seq(p, parent);
+    if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", parent);
+    if (n_shared < 0 || n_shared > s->len || n_shared % p->block_size != 0)
+        return fail(PKV_ERR_INVALID_ARG, "fork length %d must be a multiple of %d and <= parent length %d", n_shared,
+                    p->block_size, s->len);
+    if (p->next_id == std::numeric_limits<int32_t>::max()) return fail(PKV_ERR_OUT_OF_RANGE, "sequence ids exhausted");
+    Seq c;
+    try {
+        c.blocks.assign(s->blocks.begin(), s->blocks.begin() + n_shared / p->block_size);
+        c.len = n_shared;
+        const int32_t id = p->next_id;
+        p->seqs.emplace(id, std::move(c));
+        ++p->next_id;
+        for (int32_t b : p->seqs[id].blocks) ref_inc(p, b);
+        *child = id;
+    } catch (...) {
+        return fail(PKV_ERR_DEVICE, "host allocation failed");
+    }
+    return ok();
+}
+
+int kv_seq_free(kv_pool_t* p, int32_t seq) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    auto it = p->seqs.find(seq);
+    if (it == p->seqs.end()) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
+    for (int32_t b : it->second.blocks) {
+        ref_dec(p, b);
+        if (p->ref[b] == 0) p->free_list.push_back(b);
+    }
+    p->seqs.erase(it);
+    return ok();
+}
+
+int kv_seq_length(const kv_pool_t* p, int32_t seq, int32_t* len) {
+    if (!p || !len) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    const Seq* s = find_seq(p, seq);
+    if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
+    *len = s->len;
+    return ok();
+}
+
+int kv_block_tables(const kv_pool_t* p, const int32_t* seqs, int32_t n, int32_t max_blocks, int32_t* tables,
+                    int32_t* lens) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    if (n < 0 || max_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
+    if (n > 0 && (!seqs || !lens || (max_blocks > 0 && !tables))) return fail(PKV_ERR_INVALID_ARG, "NULL array");
+    for (int32_t i = 0; i < n; ++i) {
+        const Seq* s = find_seq(p, seqs[i]);
+        if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seqs[i]);
+        if ((int64_t)s->blocks.size() > max_blocks)
+            return fail(PKV_ERR_OUT_OF_RANGE, "sequence %d has %zu blocks > max_blocks_per_seq %d", seqs[i],
+                        s->blocks.size(), max_blocks);
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const Seq* s = find_seq(p, seqs[i]);
+        int32_t* row = tables + (int64_t)i * max_blocks;
+        const int32_t nb = (int32_t)s->blocks.size();
+        for (int32_t j = 0; j < nb; ++j) row[j] = s->blocks[j];
+        for (int32_t j = nb; j < max_blocks; ++j) row[j] = -1;
+        lens[i] = s->len;
+    }
+    return ok();
+}
+
+int kv_block_refcount(const kv_pool_t* p, int32_t block, int32_t* out) {
+    if (!p || !out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    if (block < 0 || block >= p->num_blocks) return fail(PKV_ERR_INVALID_ARG, "block %d out of range", block);
+    *out = p->ref[block];
+    return ok();
+}
+
+int kv_free_list(const kv_pool_t* p, int32_t* out, int32_t cap, int32_t* n) {
+    if (!p || !n) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    *n = (int32_t)p->free_list.size();
+    if (cap < *n) return fail(PKV_ERR_OUT_OF_RANGE, "capacity %d < free list length %d", cap, *n);
+    if (*n > 0 && !out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+    int32_t i = 0;
+    for (int32_t b : p->free_list) out[i++] = b;
+    return ok();
+}
+
+// ---------------------------------------------------------------- device work
+int kv_append(kv_pool_t* p, const int32_t* slot_mapping, int32_t T, const void* k_new, const void* v_new,
+              int32_t src_dtype, void* stream) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    if (T < 0) return fail(PKV_ERR_INVALID_ARG, "T < 0");
+    if (!dtype_known(src_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown src dtype %d", src_dtype);
+    const bool pairing = src_dtype == p->dtype ||
+                         (p->dtype == PKV_FP8_E4M3 && (src_dtype == PKV_BF16 || src_dtype == PKV_F32));
+    if (!pairing) return fail(PKV_ERR_UNSUPPORTED, "cannot append dtype %d into a pool of dtype %d", src_dtype, p->dtype);
+    if (T > 0 && (!slot_mapping || !k_new || !v_new)) return fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+    if (T > 0 && (!aligned16(k_new) || !aligned16(v_new))) return fail(PKV_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+    if ((int64_t)T * p->kv_heads * p->head_dim > (int64_t)1 << 40) return fail(PKV_ERR_INVALID_ARG, "T too large");
+    if (p->host_only) return fail(PKV_ERR_STATE, "host-only pool has no device memory");
+    if (T == 0) return ok();
+    pkv::AppendParams a{};
+    a.slots = slot_mapping;
+    a.k_src = k_new;
+    a.v_src = v_new;
+    a.k_pool = p->k_pool;
+    a.v_pool = p->v_pool;
+    a.k_inv = p->scales ? p->scales + 2 * p->kv_heads : nullptr;
+    a.v_inv = p->scales ? p->scales + 3 * p->kv_heads : nullptr;
+    a.num_slots = (int64_t)p->num_blocks * p->block_size;
+    a.T = T;
+    a.H_kv = p->kv_heads;
+    a.D = p->head_dim;
+    a.src_dt = src_dtype;
+    a.dst_dt = p->dtype;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = timed_launch(p, "kv_append", s, [&] { return pkv::launch_kv_append(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t resolve_partition(const kv_pool* p, int32_t B, int32_t H_q, int32_t max_len) {
+    if (max_len <= 0) return 64;
+    if (p->partition_tokens > 0) return p->partition_tokens;
+    const int64_t G = H_q / p->kv_heads;
+    const int64_t wg_cols = (int64_t)B * p->kv_heads * (G / pkv::decode_heads_per_wg((int32_t)G));
+    // Largest partition in [256, 2048] that still gives >= 4096 workgroups, so
+    // the 256 CUs stay busy; short contexts fall back to a single partition.
+    int32_t P = 2048;
+    while (P > 256 && wg_cols * ((max_len + P - 1) / P) < 4096) P /= 2;
+    if (max_len <= P) P = ((max_len + 63) / 64) * 64;
+    return P;
+}
+
+size_t workspace_for(const kv_pool* p, int32_t B, int32_t H_q, int32_t max_len, int32_t P, size_t* ml_bytes) {
+    const int64_t parts = max_len <= 0 ? 1 : (max_len + P - 1) / P;
+    if (parts <= 1) {
+        if (ml_bytes) *ml_bytes = 0;
+        return 0;
+    }
+    const size_t ml = ((size_t)B * H_q * parts * 2 * sizeof(float) + 255) & ~(size_t)255;
+    if (ml_bytes) *ml_bytes = ml;
+    return ml + (size_t)B * H_q * parts * p->head_dim * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_decode_set_partition(kv_pool_t* p, int32_t partition_tokens) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    if (partition_tokens != 0 && (partition_tokens < 64 || partition_tokens > (1 << 20) || partition_tokens % 64 != 0))
+        return fail(PKV_ERR_INVALID_ARG, "partition must be 0 or a multiple of 64 in [64, 1048576]");
+    p->partition_tokens = partition_tokens;
+    return ok();
+}
+
+int32_t paged_decode_partition_tokens(const kv_pool_t* p, int32_t B, int32_t H_q, int32_t max_context_len) {
+    if (!p || H_q <= 0 || H_q % p->kv_heads != 0) return 0;
+    return resolve_partition(p, B, H_q, max_context_len);
+}
+
+size_t paged_decode_workspace_bytes(const kv_pool_t* p, int32_t B, int32_t H_q, int32_t max_context_len) {
+    if (!p || B <= 0 || H_q <= 0 || H_q % p->kv_heads != 0) return 0;
+    return workspace_for(p, B, H_q, max_context_len, resolve_partition(p, B, H_q, max_context_len), nullptr);
+}
+
+int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_t H_q, const int32_t* block_tables,
+                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, float scale,
+                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    if (B < 0 || B > 65535) return fail(PKV_ERR_INVALID_ARG, "B must be in [0, 65535], got %d", B);
+    if (H_q <= 0 || H_q % p->kv_heads != 0)
+        return fail(PKV_ERR_INVALID_ARG, "H_q (%d) must be a positive multiple of kv_heads (%d)", H_q, p->kv_heads);
+    if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0");
+    if (max_context_len < 0) return fail(PKV_ERR_INVALID_ARG, "max_context_len < 0");
+    if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+    if (!dtype_known(q_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown q dtype %d", q_dtype);
+    const int32_t G = H_q / p->kv_heads;
+    if (!pkv::decode_supported(p->dtype, q_dtype, p->head_dim, G))
+        return fail(PKV_ERR_UNSUPPORTED, "no decode kernel for pool dtype %d, q dtype %d, head_dim %d, group %d",
+                    p->dtype, q_dtype, p->head_dim, G);
+    if ((int64_t)p->kv_heads * (G / pkv::decode_heads_per_wg(G)) > 65535)
+        return fail(PKV_ERR_INVALID_ARG, "too many query heads for one launch");
+    if (B > 0 && (!q || !out || !block_tables || !context_lens)) return fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+    if (B > 0 && (!aligned16(q) || !aligned16(out))) return fail(PKV_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
+    const int32_t max_len = (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * p->block_size);
+    const int32_t P = resolve_partition(p, B, H_q, max_len);
+    size_t ml_bytes = 0;
+    const size_t need = workspace_for(p, B, H_q, max_len, P, &ml_bytes);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (p->host_only) return fail(PKV_ERR_STATE, "host-only pool has no device memory");
+    if (B == 0) return ok();
+
+    pkv::DecodeParams d{};
+    d.k_pool = p->k_pool;
+    d.v_pool = p->v_pool;
+    d.k_scale = p->scales;
+    d.v_scale = p->scales ? p->scales + p->kv_heads : nullptr;
+    d.q = q;
+    d.out = out;
+    d.tables = block_tables;
+    d.lens = context_lens;
+    d.ws_ml = need ? reinterpret_cast<float*>(workspace) : nullptr;
+    d.ws_o = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ml_bytes) : nullptr;
+    d.B = B;
+    d.H_q = H_q;
+    d.H_kv = p->kv_heads;
+    d.G = G;
+    d.D = p->head_dim;
+    d.num_blocks = p->num_blocks;
+    d.max_blocks = max_blocks_per_seq;
+    d.max_len = max_len;
+    d.part_tokens = P;
+    d.max_parts = max_len <= 0 ? 1 : (max_len + P - 1) / P;
+    d.kv_dt = p->dtype;
+    d.q_dt = q_dtype;
+    d.scale = scale;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = timed_launch(p, "paged_decode_partition", s, [&] { return pkv::launch_decode_partition(d, s); });
+    if (e != hipSuccess) return hip_fail(e, "paged_decode_partition launch");
+    if (d.max_parts > 1) {
+        e = timed_launch(p, "paged_decode_reduce", s, [&] { return pkv::launch_decode_reduce(d, s); });
+        if (e != hipSuccess) return hip_fail(e, "paged_decode_reduce launch");
+    }
+    return ok();
+}
+
+int kv_pool_copy_to_host(const kv_pool_t* p, void* k_dst, void* v_dst) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    if (p->host_only) return fail(PKV_ERR_STATE, "host-only pool has no device memory");
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess && k_dst) e = hipMemcpy(k_dst, p->k_pool, p->pool_bytes, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && v_dst) e = hipMemcpy(v_dst, p->v_pool, p->pool_bytes, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "pool read-back");
+    return ok();
+}
+
+int pkv_profile_enable(kv_pool_t* p, int32_t on) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    if (p->host_only && on) return fail(PKV_ERR_STATE, "host-only pool launches no kernels");
+    p->profiling = on != 0;
+    return ok();
+}
+
+int pkv_profile_read(kv_pool_t* p, pkv_kernel_stat_t* out, int32_t cap, int32_t* n) {
+    if (!p || !n) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    *n = (int32_t)p->timers.size();
+    if (cap < *n) return fail(PKV_ERR_OUT_OF_RANGE, "capacity %d < %d kernels", cap, *n);
+    if (*n > 0 && !out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+    for (int32_t i = 0; i < *n; ++i) {
+        KernelTimer& t = p->timers[i];
+        double total = 0.0;
+        for (auto& ev : t.pending) {
+            float ms = 0.0f;
+            hipError_t e = hipEventSynchronize(ev.second);
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev.first, ev.second);
+            if (e != hipSuccess) return hip_fail(e, "profile event read");
+            total += ms;
+            p->spare_events.push_back(ev.first);
+            p->spare_events.push_back(ev.second);
+        }
+        std::memset(&out[i], 0, sizeof out[i]);
+        std::snprintf(out[i].name, sizeof out[i].name, "%s", t.name.c_str());
+        out[i].launches = t.launches;
+        out[i].dropped = t.dropped;
+        out[i].total_ms = total;
+        t.pending.clear();
+        t.launches = 0;
+        t.dropped = 0;
+    }
+    return ok();
+}
+
+int pkv_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!dst || !src) return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+    if (bytes % 16 || !aligned16(dst) || !aligned16(src)) return fail(PKV_ERR_INVALID_ARG, "copy needs 16-byte granularity");
+    hipError_t e = pkv::launch_copy(dst, src, bytes, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "copy launch");
+    return ok();
+}
+
+}  // extern "C"

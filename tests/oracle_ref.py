@@ -1,0 +1,53 @@
+"""Oracle expectations for a workload (test side only).
+
+The oracle never reads the device pool for attention: it regenerates each
+sequence's logical K/V from the workload's seed and runs the fp64 oracle on
+them.  For FP8 workloads it quantises the same bf16 source with its own OCP
+encoder and the same fp32 inverse scales, then attends over the dequantised
+values decode(code) * scale.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads as wl
+
+
+def fp8_codes(x_bf16_bits: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Oracle E4M3 codes of bf16 values: code = E4M3(x * fp32(1/scale)) per head (axis 1)."""
+    inv = (np.float32(1.0) / scale.astype(np.float32)).astype(np.float32)
+    x = wl.bf16_bits_to_f32(x_bf16_bits) * inv[None, :, None]
+    return oracle.e4m3_encode(x.astype(np.float32))
+
+
+def expected(w: wl.Workload, seqs=None, step: int = 0, lens_override=None, nthreads: int = 0):
+    """fp64 oracle output [len(seqs)][H_q][D] for the given sequence indices."""
+    seqs = list(range(w.B)) if seqs is None else list(seqs)
+    lens = w.lens if lens_override is None else np.asarray(lens_override, np.int32)
+    Ks, Vs, off, ln = [], [], [], []
+    t = 0
+    scales = w.fp8_scales()
+    for b in seqs:
+        n = int(lens[b])
+        K, V = w.kv(b)
+        K, V = K[:n], V[:n]
+        if w.kv_dtype == wl.E4M3:
+            K, V = fp8_codes(K, scales[0]), fp8_codes(V, scales[1])
+        Ks.append(K)
+        Vs.append(V)
+        off.append(t)
+        ln.append(n)
+        t += n
+    shape = (0, w.H_kv, w.D)
+    K = np.concatenate(Ks) if t else np.zeros(shape, wl._NP[w.kv_dtype])
+    V = np.concatenate(Vs) if t else np.zeros(shape, wl._NP[w.kv_dtype])
+    q = w.q(step)[seqs]
+    kw = {}
+    if w.kv_dtype == wl.E4M3:
+        kw = dict(k_scale=scales[0], v_scale=scales[1])
+    return oracle.decode_attention(q, w.q_dtype, K, V, w.kv_dtype, np.array(off, np.int64),
+                                   np.array(ln, np.int32), w.scale, nthreads=nthreads, **kw)
+
+
+TOL = {wl.F32: 1e-4, wl.F16: 5e-3, wl.BF16: 5e-3, wl.E4M3: 1e-2}

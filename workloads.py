@@ -18,9 +18,11 @@ Five workloads, each one decode step of one layer (block size 16):
              32768; K, V ~ N(0,1) with 0.1% elements x20, cast to bf16;
              per-kv-head scales absmax / 448; q bf16
 
-Value recipe: numpy PCG64 streams, float32 N(0,1), cast with round-to-nearest-
-even to the stored dtype.  Each sequence draws from its own spawned child
-seed, so any subset of sequences can be generated alone.  Pools hold 1.25x
+Value recipe: float32 N(0,1) from torch's CPU generator (Mersenne Twister,
+reproducible for a seed whatever the thread count), cast with round-to-
+nearest-even to the stored dtype.  Each sequence draws from its own generator,
+seeded from a numpy SeedSequence child, so any subset of sequences can be
+generated alone, and several at once on a thread pool.  Pools hold 1.25x
 the blocks the batch needs (tiny: 64, mha7b: exactly the need), and the free
 list starts as a seeded permutation, which scatters the physical blocks.
 These stand in for the Llama-2-7B / Llama-3-8B / long-tail traffic shapes the
@@ -41,28 +43,30 @@ DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", E4M3: "fp8_e4m3"}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits.
-
-    Input preparation only (the stored dtype of the bf16 workloads); finite
-    inputs are assumed, which is all the generators produce.
-    """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    return cast_to_storage(x, BF16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def cast_to_storage(x: np.ndarray, dtype: int) -> np.ndarray:
+def cast_to_storage(x, dtype: int) -> np.ndarray:
+    """float32 values (numpy or torch CPU) -> stored dtype, round to nearest even."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)) if isinstance(x, np.ndarray) else x
     if dtype == F32:
-        return np.ascontiguousarray(x, dtype=np.float32)
+        return t.to(torch.float32).numpy()
     if dtype == F16:
-        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16)
+        return t.to(torch.float16).numpy()
     if dtype == BF16:
-        return f32_to_bf16_bits(x)
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     raise ValueError("no direct cast to this storage dtype")
+
+
+def _torch_gen(ss: np.random.SeedSequence):
+    import torch
+    return torch.Generator().manual_seed(int(ss.generate_state(1, dtype=np.uint64)[0] >> 1))
 
 
 @dataclass
@@ -84,7 +88,9 @@ class Workload:
     prefix_tokens: int = 0
     outlier_p: float = 0.0
     outlier_mult: float = 1.0
+    cache_kv: bool = False   # keep generated K/V in host memory (FP8: scales need a full pass)
     _scales: tuple | None = None
+    _kv_cache: dict = field(default_factory=dict)
 
     # ------------------------------------------------------------------
     @property
@@ -116,12 +122,14 @@ class Workload:
         # children 0..B-1: sequences; B: prefix; B+1: queries; B+2..: decode-step queries
         return np.random.SeedSequence(self.seed).spawn(self.B + 2 + self.decode_steps)
 
-    def _normal(self, ss, n: int) -> np.ndarray:
-        rng = np.random.Generator(np.random.PCG64(ss))
-        x = rng.standard_normal(n, dtype=np.float32)
+    def _normal(self, ss, n: int):
+        """n float32 N(0,1) draws (torch CPU tensor); outliers x mult with prob outlier_p."""
+        import torch
+        g = _torch_gen(ss)
+        x = torch.randn(n, generator=g, dtype=torch.float32)
         if self.outlier_p > 0:
-            hit = rng.random(n, dtype=np.float32) < self.outlier_p
-            x[hit] *= np.float32(self.outlier_mult)
+            hit = torch.rand(n, generator=g, dtype=torch.float32) < self.outlier_p
+            x[hit] *= self.outlier_mult
         return x
 
     def own_tokens(self, b: int) -> int:
@@ -130,6 +138,14 @@ class Workload:
 
     def kv(self, b: int):
         """Logical (de-paged) K_b, V_b: [n_b][H_kv][D] in src_dtype storage."""
+        if b in self._kv_cache:
+            return self._kv_cache[b]
+        kv = self._kv(b)
+        if self.cache_kv:
+            self._kv_cache[b] = kv
+        return kv
+
+    def _kv(self, b: int):
         kids = self._children()
         n_own = self.own_tokens(b)
         per = self.H_kv * self.D
@@ -137,10 +153,26 @@ class Workload:
         K = x[: n_own * per].reshape(n_own, self.H_kv, self.D)
         V = x[n_own * per:].reshape(n_own, self.H_kv, self.D)
         if b in self.sharers:
+            import torch
             pK, pV = self.prefix_kv_f32(kids)
-            K = np.concatenate([pK, K])
-            V = np.concatenate([pV, V])
+            K = torch.cat([pK, K])
+            V = torch.cat([pV, V])
         return cast_to_storage(K, self.src_dtype), cast_to_storage(V, self.src_dtype)
+
+    def kv_many(self, seqs, workers: int = 8):
+        """Yield (b, K_b, V_b) in the order of `seqs`, generating ahead on a thread pool."""
+        import concurrent.futures as cf
+        seqs = list(seqs)
+        with cf.ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+            futs = {}
+            ahead = max(1, workers)
+            for i, b in enumerate(seqs[:ahead]):
+                futs[i] = ex.submit(self.kv, b)
+            for i, b in enumerate(seqs):
+                K, V = futs.pop(i).result()
+                if i + ahead < len(seqs):
+                    futs[i + ahead] = ex.submit(self.kv, seqs[i + ahead])
+                yield b, K, V
 
     def prefix_kv_f32(self, kids=None):
         kids = kids if kids is not None else self._children()
@@ -151,9 +183,10 @@ class Workload:
 
     def q(self, step: int = 0) -> np.ndarray:
         """Queries of decode step `step`: [B][H_q][D] in q_dtype storage."""
+        import torch
         kids = self._children()
-        rng = np.random.Generator(np.random.PCG64(kids[self.B + 1 + step]))
-        x = rng.standard_normal(self.B * self.H_q * self.D, dtype=np.float32)
+        x = torch.randn(self.B * self.H_q * self.D, generator=_torch_gen(kids[self.B + 1 + step]),
+                        dtype=torch.float32)
         return cast_to_storage(x.reshape(self.B, self.H_q, self.D), self.q_dtype)
 
     def fp8_scales(self):
@@ -163,10 +196,12 @@ class Workload:
         if self._scales is None:
             kmax = np.zeros(self.H_kv, np.float32)
             vmax = np.zeros(self.H_kv, np.float32)
-            for b in range(self.B):
-                K, V = self.kv(b)
-                kmax = np.maximum(kmax, np.abs(bf16_bits_to_f32(K)).max(axis=(0, 2)))
-                vmax = np.maximum(vmax, np.abs(bf16_bits_to_f32(V)).max(axis=(0, 2)))
+            import torch
+            amax = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).abs().amax(dim=(0, 2)) \
+                .to(torch.float32).numpy()
+            for b, K, V in self.kv_many(range(self.B)):
+                kmax = np.maximum(kmax, amax(K))
+                vmax = np.maximum(vmax, amax(V))
             self._scales = ((kmax / np.float32(448.0)).astype(np.float32),
                             (vmax / np.float32(448.0)).astype(np.float32))
         return self._scales
@@ -243,7 +278,7 @@ def make(name: str) -> Workload:
         nb = _pool_blocks(lens, [], 0, 1.25)
         steps, pre = 1, lens - 1
         w = Workload(name, seed, B, Hq, Hkv, D, kvd, qd, lens, nb, None, pre, steps,
-                     outlier_p=0.001, outlier_mult=20.0)
+                     outlier_p=0.001, outlier_mult=20.0, cache_kv=True)
         w.free_order = _free_order(seed, nb)
         return w
     else:
