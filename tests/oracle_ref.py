@@ -51,3 +51,21 @@ def expected(w: wl.Workload, seqs=None, step: int = 0, lens_override=None, nthre
 
 
 TOL = {wl.F32: 1e-4, wl.F16: 5e-3, wl.BF16: 5e-3, wl.E4M3: 1e-2}
+_FRAC_BITS = {wl.F32: 23, wl.F16: 10, wl.BF16: 7}
+_MIN_EXP = {wl.F32: -126, wl.F16: -14, wl.BF16: -126}
+
+
+def half_ulp(x: np.ndarray, out_dtype: int) -> np.ndarray:
+    """Half a unit in the last place of the output format at |x|: the error of
+    storing the exact result in that format, which no kernel can avoid."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.where(a > 0, np.floor(np.log2(np.where(a > 0, a, 1.0))), _MIN_EXP[out_dtype])
+    e = np.maximum(e, _MIN_EXP[out_dtype])
+    return np.ldexp(1.0, (e - _FRAC_BITS[out_dtype] - 1).astype(np.int64))
+
+
+def parity_error(got: np.ndarray, want: np.ndarray, out_dtype: int) -> float:
+    """max(|got - want| - half_ulp(want)): the error beyond the output format's own rounding."""
+    if got.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got - want) - half_ulp(want, out_dtype)))
