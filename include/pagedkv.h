@@ -154,6 +154,16 @@ int kv_seq_create(kv_pool_t* pool, int32_t* seq_id);
  * NO_BLOCKS, OUT_OF_RANGE (length beyond INT32_MAX). */
 int kv_seq_reserve(kv_pool_t* pool, int32_t seq, int32_t n_tokens, int32_t* slot_mapping_out);
 
+/* Reserve for a whole batch in one call: for i in 0..n-1, in order, reserve
+ * n_tokens[i] (n_tokens NULL: 1 each) positions for seqs[i] and write their
+ * slots consecutively to slots_out (host, sum of the counts int32).  The decode
+ * step of a batch is one such call with one token per sequence.  All or
+ * nothing over the whole batch: on NO_BLOCKS (or any error) nothing changed.
+ * A sequence may appear more than once.  Errors: as kv_seq_reserve, plus
+ * INVALID_ARG (n < 0, NULL arrays). */
+int kv_batch_reserve(kv_pool_t* pool, const int32_t* seqs, int32_t n, const int32_t* n_tokens,
+                     int32_t* slots_out);
+
 /* New sequence sharing the first n_shared_tokens of `parent` by reference:
  * the child's table points at the same n_shared/block_size physical blocks,
  * each of whose refcount is incremented ([cf1] §3.3 shared prefix; [lqnn] §3

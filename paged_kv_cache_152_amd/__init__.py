@@ -71,6 +71,7 @@ _SIGNATURES = {
     "kv_pool_set_fp8_scales": (ctypes.c_int, [_P, _P, _P]),
     "kv_seq_create": (ctypes.c_int, [_P, _PI32]),
     "kv_seq_reserve": (ctypes.c_int, [_P, _I32, _I32, _P]),
+    "kv_batch_reserve": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
     "kv_seq_fork": (ctypes.c_int, [_P, _I32, _I32, _PI32]),
     "kv_seq_free": (ctypes.c_int, [_P, _I32]),
     "kv_seq_length": (ctypes.c_int, [_P, _I32, _PI32]),
@@ -234,6 +235,20 @@ class KVPool:
         _check(lib().kv_seq_reserve(self.handle, seq, n_tokens, slots.ctypes.data_as(_P) if n_tokens > 0 else None),
                "kv_seq_reserve")
         return slots
+
+    def batch_reserve(self, seqs, n_tokens=None) -> np.ndarray:
+        """kv_batch_reserve: slots for every (sequence, count), concatenated in order."""
+        s, sp = _np_i32(seqs)
+        if n_tokens is None:
+            total, cp = len(s), None
+        else:
+            c, cp = _np_i32(n_tokens)
+            if c.shape != s.shape:
+                raise ValueError("one count per sequence")
+            total = int(c.sum())
+        slots = np.empty(max(total, 1), np.int32)
+        _check(lib().kv_batch_reserve(self.handle, sp, len(s), cp, slots.ctypes.data_as(_P)), "kv_batch_reserve")
+        return slots[:total]
 
     def seq_fork(self, parent: int, n_shared_tokens: int) -> int:
         child = ctypes.c_int32()

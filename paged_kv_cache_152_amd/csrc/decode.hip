@@ -26,6 +26,8 @@
 // the V scale multiplies the merged output.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace pkv {
 namespace {
 
@@ -133,164 +135,61 @@ __device__ __forceinline__ float row_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int KDT, int QDT, int D, int GS>
-__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(DecodeParams p) {
-    using TL = Tile<KDT, D>;
-    using RawT = typename Raw<TL::W>::T;
-    constexpr int EPL = TL::EPL, LPR = TL::LPR, RPL = TL::RPL, NLOAD = TL::NLOAD;
-    constexpr int NS = kDecodeWaves * RPL;   // softmax streams per workgroup
+// ---------------------------------------------------------------------------
+// Pieces shared by both partition kernels.
+// ---------------------------------------------------------------------------
 
-    __shared__ float s_m[NS][GS];
-    __shared__ float s_l[NS][GS];
-    __shared__ float s_o[NS][GS][D];
-
-    const int part = blockIdx.x;
-    const int subs = p.G / GS;
-    const int g = blockIdx.y / subs;
-    const int hq0 = g * p.G + (blockIdx.y % subs) * GS;
-    const int b = blockIdx.z;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int r = lane / LPR, c = lane % LPR;
-
+// Context length of sequence b, clamped to what the launch was sized for.
+__device__ __forceinline__ int clamped_len(const DecodeParams& p, int b) {
     int n = p.lens[b];
     n = n < 0 ? 0 : n;
     n = n > p.max_len ? p.max_len : n;
-    n = n > p.max_blocks * kBlock ? p.max_blocks * kBlock : n;
-    const int pstart = part * p.part_tokens;
-    const bool single = n <= p.part_tokens;
-    if (n == 0) {
-        // empty context: out = 0 (written once, by partition 0)
-        if (part == 0)
-            for (int i = tid; i < GS * D; i += kDecodeWaves * 64)
-                store_out<QDT>(p.out, ((int64_t)b * p.H_q + hq0) * D + i, 0.0f);
-        return;
+    return n > p.max_blocks * kBlock ? p.max_blocks * kBlock : n;
+}
+
+__device__ __forceinline__ int num_parts(const DecodeParams& p, int n) {
+    return (n + p.part_tokens - 1) / p.part_tokens;
+}
+
+// The k = ceil(n / P) partitions of a sequence split its blocks evenly:
+// partition i covers blocks [i*nb/k, (i+1)*nb/k), so no partition is a small
+// remainder and every one holds at most about P tokens.
+struct Range {
+    int n, nparts, blk_first, blk_last, pend;
+};
+
+__device__ __forceinline__ Range partition_range(const DecodeParams& p, int b, int part) {
+    Range R;
+    R.n = clamped_len(p, b);
+    R.nparts = num_parts(p, R.n);
+    const int nb = (R.n + kBlock - 1) / kBlock;
+    R.blk_first = (int)((int64_t)part * nb / max(R.nparts, 1));
+    R.blk_last = (int)((int64_t)(part + 1) * nb / max(R.nparts, 1));
+    R.pend = min(R.n, R.blk_last * kBlock);
+    return R;
+}
+
+// The physical block ids of one wave's blocks (blk0, blk0 + 4, ...), 64 at a
+// time, one entry per lane, fetched with a single vector load and read back
+// with readlane.  Loading them up front keeps the table lookups off the path
+// between one block's K/V loads and the next.
+struct WaveTable {
+    int v = -1;
+    __device__ __forceinline__ void load(const int32_t* table, int blk0, int nmine, int j0, int lane) {
+        const int j = j0 + lane;
+        v = j < nmine ? table[blk0 + kDecodeWaves * j] : -1;
     }
-    if (pstart >= n) return;
-    const int pend = min(n, pstart + p.part_tokens);
-    const int blk_first = pstart / kBlock;
-    const int blk_last = (pend + kBlock - 1) / kBlock;   // exclusive
+    __device__ __forceinline__ int phys(int j) const { return __builtin_amdgcn_readlane(v, j & 63); }
+};
 
-    // Query fragment: this lane's EPL dims of each of the GS heads, scaled to base 2.
-    float qscale = p.scale * kLog2e;
-    if constexpr (KDT == DT_FP8) qscale *= p.k_scale[g];
-    float qf[GS][EPL];
-#pragma unroll
-    for (int h = 0; h < GS; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            qf[h][e] = load_q<QDT>(p.q, ((int64_t)b * p.H_q + hq0 + h) * D + c * EPL + e) * qscale;
-
-    float m[GS], l[GS], acc[GS][EPL];
-#pragma unroll
-    for (int h = 0; h < GS; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
-    }
-
-    const int32_t* table = p.tables + (int64_t)b * p.max_blocks;
-    const char* kbase = reinterpret_cast<const char*>(p.k_pool);
-    const char* vbase = reinterpret_cast<const char*>(p.v_pool);
-    const int lane_off = r * NLOAD * TL::ROW + c * TL::W;
-    const int64_t head_off = (int64_t)g * TL::BYTES;
-    const int64_t blk_stride = (int64_t)p.H_kv * TL::BYTES;
-
-    RawT kc[NLOAD], vc[NLOAD], kn[NLOAD], vn[NLOAD];
-    auto fetch = [&](int blk, RawT* kr, RawT* vr) -> bool {
-        const int phys = table[blk];
-        if (phys < 0 || phys >= p.num_blocks) return false;
-        const int64_t off = (int64_t)phys * blk_stride + head_off + lane_off;
-        const char* kp = kbase + off;
-        const char* vp = vbase + off;
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            kr[i] = *reinterpret_cast<const RawT*>(kp + i * TL::ROW);
-            vr[i] = *reinterpret_cast<const RawT*>(vp + i * TL::ROW);
-        }
-        return true;
-    };
-
-    int blk = blk_first + wave;
-    bool ok_c = blk < blk_last ? fetch(blk, kc, vc) : false;
-    for (; blk < blk_last; blk += kDecodeWaves) {
-        const int nblk = blk + kDecodeWaves;
-        const bool ok_n = nblk < blk_last ? fetch(nblk, kn, vn) : false;
-        if (ok_c) {
-            const int tok0 = blk * kBlock + r * NLOAD;   // this row's first token in the block
-            const bool partial = blk * kBlock + kBlock > pend;
-            float z[GS][NLOAD];
-            float vf[NLOAD][EPL];
-#pragma unroll
-            for (int i = 0; i < NLOAD; ++i) {
-                float kf[EPL];
-                widen<KDT, TL::W>(kc[i], kf);
-                widen<KDT, TL::W>(vc[i], vf[i]);
-                const bool valid = !partial || (tok0 + i < pend);
-#pragma unroll
-                for (int h = 0; h < GS; ++h) {
-                    float d = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) d = fmaf(qf[h][e], kf[e], d);
-                    d = row_sum<LPR>(d);
-                    z[h][i] = valid ? d : -INFINITY;
-                }
-                if (partial && !valid) {
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) vf[i][e] = 0.0f;   // select, never 0 * garbage
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < GS; ++h) {
-                float mx = z[h][0];
-#pragma unroll
-                for (int i = 1; i < NLOAD; ++i) mx = fmaxf(mx, z[h][i]);
-                const float m_new = fmaxf(m[h], mx);
-                const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-                const float alpha = fast_exp2(m[h] - m_use);
-                float psum = 0.0f;
-                float pv[NLOAD];
-#pragma unroll
-                for (int i = 0; i < NLOAD; ++i) {
-                    pv[i] = fast_exp2(z[h][i] - m_use);
-                    psum += pv[i];
-                }
-                l[h] = fmaf(l[h], alpha, psum);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    float a = acc[h][e] * alpha;
-#pragma unroll
-                    for (int i = 0; i < NLOAD; ++i) a = fmaf(pv[i], vf[i][e], a);
-                    acc[h][e] = a;
-                }
-                m[h] = m_new;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            kc[i] = kn[i];
-            vc[i] = vn[i];
-        }
-        ok_c = ok_n;
-    }
-
-    // Merge the NS streams of this workgroup.
-    const int s = wave * RPL + r;
-#pragma unroll
-    for (int h = 0; h < GS; ++h) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s_o[s][h][c * EPL + e] = acc[h][e];
-        if (c == 0) {
-            s_m[s][h] = m[h];
-            s_l[s][h] = l[h];
-        }
-    }
-    __syncthreads();
-
-    float vscale = 1.0f;
-    if constexpr (KDT == DT_FP8) vscale = p.v_scale[g];
-    for (int i = tid; i < GS * D; i += kDecodeWaves * 64) {
+// Merge the NS softmax streams of a workgroup (per head: running max s_m,
+// running sum s_l, unnormalised accumulator s_o) and write either the final
+// output (one partition) or the partition's (m, l, o) for the reduce kernel.
+template <int QDT, int D, int GS, int NS>
+__device__ __forceinline__ void merge_streams(const DecodeParams& p, const float (*s_m)[GS],
+                                              const float (*s_l)[GS], const float (*s_o)[GS][D], int b,
+                                              int hq0, int part, bool single, float vscale) {
+    for (int i = threadIdx.x; i < GS * D; i += kDecodeWaves * 64) {
         const int h = i / D, d = i % D;
         float M = -INFINITY;
         for (int t = 0; t < NS; ++t) M = fmaxf(M, s_m[t][h]);
@@ -317,32 +216,475 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(Deco
     }
 }
 
+template <int QDT, int D, int GS>
+__device__ __forceinline__ void zero_output(const DecodeParams& p, int b, int hq0) {
+    for (int i = threadIdx.x; i < GS * D; i += kDecodeWaves * 64)
+        store_out<QDT>(p.out, ((int64_t)b * p.H_q + hq0) * D + i, 0.0f);
+}
+
+// Walk this wave's blocks j = 0 .. nmine-1 with two buffers: block j+1's loads
+// are in flight while block j is consumed, and no registers are copied.
+// fetch(j, buf) issues the loads; consume(j, buf, masked) uses them.
+template <class Buf, class Fetch, class Consume>
+__device__ __forceinline__ void ping_pong(int nmine, Fetch&& fetch, Consume&& consume) {
+    Buf b0, b1;
+    if (nmine > 0) fetch(0, b0);
+    int j = 0;
+    while (j < nmine) {
+        if (j + 1 < nmine) fetch(j + 1, b1);
+        consume(j, b0);
+        if (++j >= nmine) break;
+        if (j + 1 < nmine) fetch(j + 1, b0);
+        consume(j, b1);
+        ++j;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Vector variant: any dtype, head_dim 16/64/128, any group size up to 8.
+// ---------------------------------------------------------------------------
+template <int KDT, int QDT, int D, int GS>
+__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(DecodeParams p) {
+    using TL = Tile<KDT, D>;
+    using RawT = typename Raw<TL::W>::T;
+    constexpr int EPL = TL::EPL, LPR = TL::LPR, RPL = TL::RPL, NLOAD = TL::NLOAD;
+    constexpr int NS = kDecodeWaves * RPL;   // softmax streams per workgroup
+
+    __shared__ float s_m[NS][GS];
+    __shared__ float s_l[NS][GS];
+    __shared__ float s_o[NS][GS][D];
+
+    const int part = blockIdx.x;
+    const int subs = p.G / GS;
+    const int g = blockIdx.y / subs;
+    const int hq0 = g * p.G + (blockIdx.y % subs) * GS;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r = lane / LPR, c = lane % LPR;
+
+    const Range R = partition_range(p, b, part);
+    if (R.n == 0) {                      // empty context: out = 0, written by partition 0
+        if (part == 0) zero_output<QDT, D, GS>(p, b, hq0);
+        return;
+    }
+    if (part >= R.nparts) return;
+
+    // Query fragment: this lane's EPL dims of each of the GS heads, scaled to base 2.
+    float qscale = p.scale * kLog2e;
+    if constexpr (KDT == DT_FP8) qscale *= p.k_scale[g];
+    float qf[GS][EPL];
+#pragma unroll
+    for (int h = 0; h < GS; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            qf[h][e] = load_q<QDT>(p.q, ((int64_t)b * p.H_q + hq0 + h) * D + c * EPL + e) * qscale;
+
+    float m[GS], l[GS], acc[GS][EPL];
+#pragma unroll
+    for (int h = 0; h < GS; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+    }
+
+    const int32_t* table = p.tables + (int64_t)b * p.max_blocks;
+    const char* kbase = reinterpret_cast<const char*>(p.k_pool);
+    const char* vbase = reinterpret_cast<const char*>(p.v_pool);
+    const int lane_off = r * NLOAD * TL::ROW + c * TL::W;
+    const int64_t head_off = (int64_t)g * TL::BYTES;
+    const int64_t blk_stride = (int64_t)p.H_kv * TL::BYTES;
+    const int blk0 = R.blk_first + wave;
+    const int nmine = blk0 < R.blk_last ? (R.blk_last - blk0 + kDecodeWaves - 1) / kDecodeWaves : 0;
+    WaveTable wt;
+    wt.load(table, blk0, nmine, 0, lane);
+
+    struct Buf {
+        RawT k[NLOAD], v[NLOAD];
+        bool ok;
+    };
+    auto fetch = [&](int j, Buf& B) {
+        if ((j & 63) == 0 && j > 0) wt.load(table, blk0, nmine, j, lane);
+        const int phys = wt.phys(j);
+        B.ok = phys >= 0 && phys < p.num_blocks;
+        if (!B.ok) return;
+        const int64_t off = (int64_t)phys * blk_stride + head_off + lane_off;
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            B.k[i] = *reinterpret_cast<const RawT*>(kbase + off + i * TL::ROW);
+            B.v[i] = *reinterpret_cast<const RawT*>(vbase + off + i * TL::ROW);
+        }
+    };
+    auto update = [&](auto masked, int blk, const Buf& B) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const int tok0 = blk * kBlock + r * NLOAD;   // this row's first token in the block
+        float z[GS][NLOAD];
+        float vf[NLOAD][EPL];
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            float kf[EPL];
+            widen<KDT, TL::W>(B.k[i], kf);
+            widen<KDT, TL::W>(B.v[i], vf[i]);
+            const bool valid = !MASKED || tok0 + i < R.pend;
+#pragma unroll
+            for (int h = 0; h < GS; ++h) {
+                float d = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) d = fmaf(qf[h][e], kf[e], d);
+                d = row_sum<LPR>(d);
+                z[h][i] = valid ? d : -INFINITY;
+            }
+            if (MASKED && !valid) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) vf[i][e] = 0.0f;   // select, never 0 * garbage
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < GS; ++h) {
+            float mx = z[h][0];
+#pragma unroll
+            for (int i = 1; i < NLOAD; ++i) mx = fmaxf(mx, z[h][i]);
+            const float m_new = fmaxf(m[h], mx);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = fast_exp2(m[h] - m_use);
+            float psum = 0.0f;
+            float pv[NLOAD];
+#pragma unroll
+            for (int i = 0; i < NLOAD; ++i) {
+                pv[i] = fast_exp2(z[h][i] - m_use);
+                psum += pv[i];
+            }
+            l[h] = fmaf(l[h], alpha, psum);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                float a = acc[h][e] * alpha;
+#pragma unroll
+                for (int i = 0; i < NLOAD; ++i) a = fmaf(pv[i], vf[i][e], a);
+                acc[h][e] = a;
+            }
+            m[h] = m_new;
+        }
+    };
+    auto consume = [&](int j, const Buf& B) {
+        if (!B.ok) return;
+        const int blk = blk0 + kDecodeWaves * j;
+        if (blk * kBlock + kBlock > R.pend) update(std::integral_constant<bool, true>{}, blk, B);
+        else update(std::integral_constant<bool, false>{}, blk, B);
+    };
+    ping_pong<Buf>(nmine, fetch, consume);
+
+    const int s = wave * RPL + r;
+#pragma unroll
+    for (int h = 0; h < GS; ++h) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_o[s][h][c * EPL + e] = acc[h][e];
+        if (c == 0) {
+            s_m[s][h] = m[h];
+            s_l[s][h] = l[h];
+        }
+    }
+    __syncthreads();
+    float vscale = 1.0f;
+    if constexpr (KDT == DT_FP8) vscale = p.v_scale[g];
+    merge_streams<QDT, D, GS, NS>(p, s_m, s_l, s_o, b, hq0, part, R.nparts == 1, vscale);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped-query variant (GS >= 3 query heads per KV head, head_dim 128,
+// 16-bit or FP8 KV): Q.K^T on the matrix cores, P.V on the vector ALUs.
+//
+// Per 16-token block a wave issues KS = 4 v_mfma_f32_16x16x32 (bf16 or f16):
+// A = the K tile (16 tokens x 32 dims per step), B = the queries (32 dims x 16
+// head columns, GS of them live, the rest zero).  Lane l supplies A row
+// m = l % 16 (a token) and B column n = l % 16 (a head), both for the dim group
+// 8 * (4 s + l / 16) .. +7 of step s, so each lane's A operand is one 16-byte
+// (8-byte for FP8) load of a token row.  The 16x16 fp32 result leaves scores
+// of tokens 4r .. 4r+3 for head n in lane 16r + n (r = l / 16): exactly the
+// tokens whose V rows the lanes of DPP row r load for the P.V update, so each
+// head's weight reaches its row with one row_newbcast and every lane
+// accumulates 8 output dims for all GS heads.  Each lane (r, n) keeps the
+// running max / sum of stream (r, head n); the accumulators of stream (r, h)
+// are spread over the 16 lanes of row r.  An FP8 tile is widened to bf16/f16
+// (exact) for the MFMA and to fp32 for P.V.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+template <int QDT> struct MfmaIn;
+template <> struct MfmaIn<DT_BF16> { using T = bf16x8_t; };
+template <> struct MfmaIn<DT_F16> { using T = f16x8_t; };
+
+template <int QDT>
+__device__ __forceinline__ f32x4_t mfma16x16x32(const typename MfmaIn<QDT>::T& a, const typename MfmaIn<QDT>::T& b,
+                                                f32x4_t c) {
+    if constexpr (QDT == DT_BF16) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 8 E4M3 codes (two words) -> 8 bf16 / f16 values, exact.
+template <int QDT>
+__device__ __forceinline__ typename MfmaIn<QDT>::T fp8x8_to_mfma(uint2 w) {
+    uint32_t o[4];
+    if constexpr (QDT == DT_BF16) {
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+    } else {
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true));
+    }
+    return __builtin_bit_cast(typename MfmaIn<QDT>::T, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+__device__ __forceinline__ float row_bcast(float v, int src_lane_in_row) {
+    // DPP row_newbcast: every lane of a 16-lane row receives lane `src` of that row.
+    switch (src_lane_in_row) {
+        case 0: return __builtin_amdgcn_update_dpp(0.0f, v, 0x150, 0xF, 0xF, false);
+        case 1: return __builtin_amdgcn_update_dpp(0.0f, v, 0x151, 0xF, 0xF, false);
+        case 2: return __builtin_amdgcn_update_dpp(0.0f, v, 0x152, 0xF, 0xF, false);
+        case 3: return __builtin_amdgcn_update_dpp(0.0f, v, 0x153, 0xF, 0xF, false);
+        case 4: return __builtin_amdgcn_update_dpp(0.0f, v, 0x154, 0xF, 0xF, false);
+        case 5: return __builtin_amdgcn_update_dpp(0.0f, v, 0x155, 0xF, 0xF, false);
+        case 6: return __builtin_amdgcn_update_dpp(0.0f, v, 0x156, 0xF, 0xF, false);
+        default: return __builtin_amdgcn_update_dpp(0.0f, v, 0x157, 0xF, 0xF, false);
+    }
+}
+
+template <int KDT>
+struct GqaTile {
+    static constexpr int E = Elem<KDT>::bytes;
+    static constexpr int ROW = 128 * E;                  // bytes of a token row
+    static constexpr int BYTES = kBlock * ROW;
+    static constexpr int KW = 8 * E;                      // bytes per lane per MFMA step (8 dims)
+    using KRaw = typename Raw<KW>::T;                     // uint4 (16-bit) or uint2 (FP8)
+    using VRaw = typename Raw<KW>::T;
+};
+
+template <int KDT, int QDT, int GS>
+__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition_gqa(DecodeParams p) {
+    constexpr int D = 128, KS = 4, NS = kDecodeWaves * 4;
+    using TL = GqaTile<KDT>;
+    using KRaw = typename TL::KRaw;
+    using MT = typename MfmaIn<QDT>::T;
+
+    __shared__ float s_m[NS][GS];
+    __shared__ float s_l[NS][GS];
+    __shared__ float s_o[NS][GS][D];
+
+    const int part = blockIdx.x;
+    const int subs = p.G / GS;
+    const int g = blockIdx.y / subs;
+    const int hq0 = g * p.G + (blockIdx.y % subs) * GS;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r = lane >> 4, c = lane & 15;      // DPP row; lane within the row
+
+    const Range R = partition_range(p, b, part);
+    if (R.n == 0) {
+        if (part == 0) zero_output<QDT, D, GS>(p, b, hq0);
+        return;
+    }
+    if (part >= R.nparts) return;
+
+    // B operand: head c (zero beyond GS), dims 8 * (4 s + r) .. +7 for step s.
+    MT qb[KS];
+    {
+        const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+            if (c < GS)
+                raw = *reinterpret_cast<const uint4*>(q16 + ((int64_t)b * p.H_q + hq0 + c) * D + 8 * (4 * s + r));
+            qb[s] = __builtin_bit_cast(MT, raw);
+        }
+    }
+    float qscale = p.scale * kLog2e;
+    if constexpr (KDT == DT_FP8) qscale *= p.k_scale[g];
+
+    float m_run = -INFINITY, l_run = 0.0f;   // stream (row r, head c)
+    float acc[GS][8];
+#pragma unroll
+    for (int h = 0; h < GS; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+
+    const int32_t* table = p.tables + (int64_t)b * p.max_blocks;
+    const char* kbase = reinterpret_cast<const char*>(p.k_pool);
+    const char* vbase = reinterpret_cast<const char*>(p.v_pool);
+    const int64_t head_off = (int64_t)g * TL::BYTES;
+    const int64_t blk_stride = (int64_t)p.H_kv * TL::BYTES;
+    // K: token c, step s -> bytes KW * (4 s + r); V: token 4 r + i, bytes KW * c.
+    const int k_off = c * TL::ROW + r * TL::KW;
+    const int v_off = (4 * r) * TL::ROW + c * TL::KW;
+    const int blk0 = R.blk_first + wave;
+    const int nmine = blk0 < R.blk_last ? (R.blk_last - blk0 + kDecodeWaves - 1) / kDecodeWaves : 0;
+    WaveTable wt;
+    wt.load(table, blk0, nmine, 0, lane);
+
+    struct Buf {
+        KRaw k[KS];
+        KRaw v[4];
+        bool ok;
+    };
+    auto fetch = [&](int j, Buf& B) {
+        if ((j & 63) == 0 && j > 0) wt.load(table, blk0, nmine, j, lane);
+        const int phys = wt.phys(j);
+        B.ok = phys >= 0 && phys < p.num_blocks;
+        if (!B.ok) return;
+        const int64_t off = (int64_t)phys * blk_stride + head_off;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) B.k[s] = *reinterpret_cast<const KRaw*>(kbase + off + k_off + s * 4 * TL::KW);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) B.v[i] = *reinterpret_cast<const KRaw*>(vbase + off + v_off + i * TL::ROW);
+    };
+    auto update = [&](auto masked, int blk, const Buf& B) {
+        constexpr bool MASKED = decltype(masked)::value;
+        f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            MT a;
+            if constexpr (KDT == DT_FP8) a = fp8x8_to_mfma<QDT>(B.k[s]);
+            else a = __builtin_bit_cast(MT, B.k[s]);
+            S = mfma16x16x32<QDT>(a, qb[s], S);
+        }
+        const int tok = blk * kBlock + 4 * r;           // token of S[0] in this lane
+        float z[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z[i] = S[i] * qscale;
+            if (MASKED && tok + i >= R.pend) z[i] = -INFINITY;
+        }
+        const float m_new = fmaxf(fmaxf(m_run, fmaxf(z[0], z[1])), fmaxf(z[2], z[3]));
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(z[i] - m_use);
+        l_run = fmaf(l_run, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
+        m_run = m_new;
+        // rescale the accumulators of every stream whose max moved
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f && c < GS) != 0) {
+#pragma unroll
+            for (int h = 0; h < GS; ++h) {
+                const float ah = row_bcast(alpha, h);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float vf[8];
+            widen<KDT, TL::KW>(B.v[i], vf);
+            if (MASKED && tok + i >= R.pend) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vf[e] = 0.0f;   // select, never 0 * garbage
+            }
+#pragma unroll
+            for (int h = 0; h < GS; ++h) {
+                const float ph = row_bcast(pr[i], h);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+            }
+        }
+    };
+    auto consume = [&](int j, const Buf& B) {
+        if (!B.ok) return;
+        const int blk = blk0 + kDecodeWaves * j;
+        if (blk * kBlock + kBlock > R.pend) update(std::integral_constant<bool, true>{}, blk, B);
+        else update(std::integral_constant<bool, false>{}, blk, B);
+    };
+    ping_pong<Buf>(nmine, fetch, consume);
+
+    // Merge the 16 streams (4 waves x 4 rows) of each head through LDS.
+    const int srow = wave * 4 + r;
+    if (c < GS) {
+        s_m[srow][c] = m_run;
+        s_l[srow][c] = l_run;
+    }
+#pragma unroll
+    for (int h = 0; h < GS; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_o[srow][h][c * 8 + e] = acc[h][e];
+    __syncthreads();
+    float vscale = 1.0f;
+    if constexpr (KDT == DT_FP8) vscale = p.v_scale[g];
+    merge_streams<QDT, D, GS, NS>(p, s_m, s_l, s_o, b, hq0, part, R.nparts == 1, vscale);
+}
+
+// Wave-wide max / sum; every lane gets the same value (fixed butterfly order).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float lane_bcast(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 // Kernel 2: merge the partitions of one (sequence, query head) with the same
 // rule as the in-workgroup merge: M = max m_t, L = sum l_t 2^(m_t - M),
 // out = sum o_t 2^(m_t - M) / L.  Sequences that fit one partition were
-// finished by kernel 1 and are skipped here.
-template <int QDT>
+// finished by kernel 1 and are skipped here.  Lane t handles partition t's
+// (m, l) (64 partitions per sweep); the weights are broadcast from their lanes
+// while every lane accumulates its own output dims, so the partial-output
+// loads are independent of each other.
+template <int QDT, int D>
 __global__ __launch_bounds__(64) void paged_decode_reduce(DecodeParams p) {
+    constexpr int DPL = D >= 64 ? D / 64 : 1;      // output dims per lane
     const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    int n = p.lens[b];
-    n = n < 0 ? 0 : n;
-    n = n > p.max_len ? p.max_len : n;
-    n = n > p.max_blocks * kBlock ? p.max_blocks * kBlock : n;
-    const int nparts = (n + p.part_tokens - 1) / p.part_tokens;
+    const int nparts = num_parts(p, clamped_len(p, b));
     if (nparts <= 1) return;
     const int64_t base = ((int64_t)b * p.H_q + hq) * p.max_parts;
+    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + base;
+    const float* po = p.ws_o + base * D;
+
     float M = -INFINITY;
-    for (int t = 0; t < nparts; ++t) M = fmaxf(M, p.ws_ml[(base + t) * 2]);
-    for (int d = lane; d < p.D; d += 64) {
-        float L = 0.0f, O = 0.0f;
-        if (M != -INFINITY) {
-            for (int t = 0; t < nparts; ++t) {
-                const float w = fast_exp2(p.ws_ml[(base + t) * 2] - M);
-                L = fmaf(p.ws_ml[(base + t) * 2 + 1], w, L);
-                O = fmaf(p.ws_o[(base + t) * p.D + d], w, O);
+    for (int t0 = 0; t0 < nparts; t0 += 64)
+        if (t0 + lane < nparts) M = fmaxf(M, ml[t0 + lane].x);
+    M = wave_max(M);
+
+    float L = 0.0f, o[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) o[i] = 0.0f;
+    const bool live = D >= 64 || lane < D;
+    if (M != -INFINITY) {
+        for (int t0 = 0; t0 < nparts; t0 += 64) {
+            const int t = t0 + lane;
+            float w = 0.0f;
+            if (t < nparts) {
+                const float2 v = ml[t];
+                w = fast_exp2(v.x - M);
+                L = fmaf(v.y, w, L);
+            }
+            const int cnt = min(64, nparts - t0);
+#pragma unroll 8
+            for (int j = 0; j < cnt; ++j) {
+                const float wj = lane_bcast(w, j);
+                const float* src = po + (int64_t)(t0 + j) * D;
+                if (live) {
+#pragma unroll
+                    for (int i = 0; i < DPL; ++i) o[i] = fmaf(src[lane + 64 * i], wj, o[i]);
+                }
             }
         }
-        store_out<QDT>(p.out, ((int64_t)b * p.H_q + hq) * p.D + d, L > 0.0f ? O / L : 0.0f);
+    }
+    L = wave_sum(L);
+    if (live) {
+#pragma unroll
+        for (int i = 0; i < DPL; ++i)
+            store_out<QDT>(p.out, ((int64_t)b * p.H_q + hq) * D + lane + 64 * i, L > 0.0f ? o[i] / L : 0.0f);
     }
 }
 
@@ -350,17 +692,27 @@ using KernelFn = void (*)(DecodeParams);
 
 template <int KDT, int QDT, int D>
 KernelFn pick_gs(int gs) {
+    // groups >= 3 at head_dim 128 with 16-bit / FP8 storage always take the
+    // matrix-core variant; do not instantiate vector kernels for them
+    constexpr bool kGqaCovers = D == 128 && KDT != DT_F32;
+    if (kGqaCovers && gs >= 3) return nullptr;
     switch (gs) {
         case 1: return paged_decode_partition<KDT, QDT, D, 1>;
         case 2: return paged_decode_partition<KDT, QDT, D, 2>;
-        case 3: return paged_decode_partition<KDT, QDT, D, 3>;
-        case 4: return paged_decode_partition<KDT, QDT, D, 4>;
-        case 5: return paged_decode_partition<KDT, QDT, D, 5>;
-        case 6: return paged_decode_partition<KDT, QDT, D, 6>;
-        case 7: return paged_decode_partition<KDT, QDT, D, 7>;
-        case 8: return paged_decode_partition<KDT, QDT, D, 8>;
-        default: return nullptr;
+        default: break;
     }
+    if constexpr (!kGqaCovers) {
+        switch (gs) {
+            case 3: return paged_decode_partition<KDT, QDT, D, 3>;
+            case 4: return paged_decode_partition<KDT, QDT, D, 4>;
+            case 5: return paged_decode_partition<KDT, QDT, D, 5>;
+            case 6: return paged_decode_partition<KDT, QDT, D, 6>;
+            case 7: return paged_decode_partition<KDT, QDT, D, 7>;
+            case 8: return paged_decode_partition<KDT, QDT, D, 8>;
+            default: return nullptr;
+        }
+    }
+    return nullptr;
 }
 
 template <int KDT, int QDT>
@@ -373,7 +725,34 @@ KernelFn pick_d(int D, int gs) {
     }
 }
 
+KernelFn pick_vector(int kdt, int qdt, int D, int gs);
+
+template <int KDT, int QDT>
+KernelFn pick_gqa(int gs) {
+    switch (gs) {
+        case 3: return paged_decode_partition_gqa<KDT, QDT, 3>;
+        case 4: return paged_decode_partition_gqa<KDT, QDT, 4>;
+        case 5: return paged_decode_partition_gqa<KDT, QDT, 5>;
+        case 6: return paged_decode_partition_gqa<KDT, QDT, 6>;
+        case 7: return paged_decode_partition_gqa<KDT, QDT, 7>;
+        case 8: return paged_decode_partition_gqa<KDT, QDT, 8>;
+        default: return nullptr;
+    }
+}
+
+// Grouped heads with 128-dim heads and 16-bit / FP8 storage take the matrix-core
+// variant; everything else the vector variant.
 KernelFn pick_partition(int kdt, int qdt, int D, int gs) {
+    if (D == 128 && gs >= 3) {
+        if (kdt == DT_F16 && qdt == DT_F16) return pick_gqa<DT_F16, DT_F16>(gs);
+        if (kdt == DT_BF16 && qdt == DT_BF16) return pick_gqa<DT_BF16, DT_BF16>(gs);
+        if (kdt == DT_FP8 && qdt == DT_BF16) return pick_gqa<DT_FP8, DT_BF16>(gs);
+        if (kdt == DT_FP8 && qdt == DT_F16) return pick_gqa<DT_FP8, DT_F16>(gs);
+    }
+    return pick_vector(kdt, qdt, D, gs);
+}
+
+KernelFn pick_vector(int kdt, int qdt, int D, int gs) {
     if (kdt == DT_F32 && qdt == DT_F32) return pick_d<DT_F32, DT_F32>(D, gs);
     if (kdt == DT_F16 && qdt == DT_F16) return pick_d<DT_F16, DT_F16>(D, gs);
     if (kdt == DT_BF16 && qdt == DT_BF16) return pick_d<DT_BF16, DT_BF16>(D, gs);
@@ -382,11 +761,21 @@ KernelFn pick_partition(int kdt, int qdt, int D, int gs) {
     return nullptr;
 }
 
-KernelFn pick_reduce(int qdt) {
+template <int QDT>
+KernelFn pick_reduce_d(int D) {
+    switch (D) {
+        case 16: return paged_decode_reduce<QDT, 16>;
+        case 64: return paged_decode_reduce<QDT, 64>;
+        case 128: return paged_decode_reduce<QDT, 128>;
+        default: return nullptr;
+    }
+}
+
+KernelFn pick_reduce(int qdt, int D) {
     switch (qdt) {
-        case DT_F32: return paged_decode_reduce<DT_F32>;
-        case DT_F16: return paged_decode_reduce<DT_F16>;
-        case DT_BF16: return paged_decode_reduce<DT_BF16>;
+        case DT_F32: return pick_reduce_d<DT_F32>(D);
+        case DT_F16: return pick_reduce_d<DT_F16>(D);
+        case DT_BF16: return pick_reduce_d<DT_BF16>(D);
         default: return nullptr;
     }
 }
@@ -403,7 +792,7 @@ int decode_heads_per_wg(int32_t G) {
 bool decode_supported(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G) {
     if (G < 1) return false;
     return pick_partition(kv_dt, q_dt, D, decode_heads_per_wg(G)) != nullptr &&
-           pick_reduce(q_dt) != nullptr;
+           pick_reduce(q_dt, D) != nullptr;
 }
 
 hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream) {
@@ -418,7 +807,7 @@ hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {
-    KernelFn fn = pick_reduce(p.q_dt);
+    KernelFn fn = pick_reduce(p.q_dt, p.D);
     if (!fn) return hipErrorInvalidValue;
     DecodeParams arg = p;
     void* args[] = {&arg};

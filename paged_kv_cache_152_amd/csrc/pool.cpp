@@ -356,6 +356,45 @@ int kv_seq_reserve(kv_pool_t* p, int32_t seq, int32_t n_tokens, int32_t* slots) 
     return ok();
 }
 
+int kv_batch_reserve(kv_pool_t* p, const int32_t* seqs, int32_t n, const int32_t* n_tokens, int32_t* slots) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n < 0");
+    if (n == 0) return ok();
+    if (!seqs || !slots) return fail(PKV_ERR_INVALID_ARG, "NULL array");
+    const int bs = p->block_size;
+    // Dry run: lengths after each request (sequences may repeat), total blocks needed.
+    int64_t need = 0;
+    try {
+        std::unordered_map<int32_t, int64_t> len;
+        for (int32_t i = 0; i < n; ++i) {
+            const int32_t k = n_tokens ? n_tokens[i] : 1;
+            if (k < 0) return fail(PKV_ERR_INVALID_ARG, "n_tokens[%d] < 0", i);
+            const Seq* s = find_seq(p, seqs[i]);
+            if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seqs[i]);
+            auto it = len.find(seqs[i]);
+            const int64_t cur = it == len.end() ? s->len : it->second;
+            const int64_t nxt = cur + k;
+            if (nxt > std::numeric_limits<int32_t>::max()) return fail(PKV_ERR_OUT_OF_RANGE, "sequence length overflow");
+            if (k > 0 && cur == s->len && cur % bs != 0 && p->ref[s->blocks.back()] != 1)
+                return fail(PKV_ERR_STATE, "would write into a shared block");
+            need += (nxt + bs - 1) / bs - (cur + bs - 1) / bs;
+            len[seqs[i]] = nxt;
+        }
+    } catch (...) {
+        return fail(PKV_ERR_DEVICE, "host allocation failed");
+    }
+    if (need > (int64_t)p->free_list.size())
+        return fail(PKV_ERR_NO_BLOCKS, "batch needs %lld blocks, %zu free", (long long)need, p->free_list.size());
+    int64_t o = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t k = n_tokens ? n_tokens[i] : 1;
+        const int rc = kv_seq_reserve(p, seqs[i], k, slots + o);
+        if (rc != PKV_OK) return rc;   // unreachable: the dry run checked every condition
+        o += k;
+    }
+    return ok();
+}
+
 int kv_seq_fork(kv_pool_t* p, int32_t parent, int32_t n_shared, int32_t* child) {
     if (!p || !child) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
     Seq* s = find_seq(p, parent);
@@ -482,10 +521,11 @@ int32_t resolve_partition(const kv_pool* p, int32_t B, int32_t H_q, int32_t max_
     if (p->partition_tokens > 0) return p->partition_tokens;
     const int64_t G = H_q / p->kv_heads;
     const int64_t wg_cols = (int64_t)B * p->kv_heads * (G / pkv::decode_heads_per_wg((int32_t)G));
-    // Largest partition in [256, 2048] that still gives >= 4096 workgroups, so
-    // the 256 CUs stay busy; short contexts fall back to a single partition.
+    // Largest partition in [256, 2048] that still gives >= 2048 workgroups
+    // (8 per CU), so the 256 CUs stay busy without making any one workgroup long
+    // enough to dominate the tail; short contexts take a single partition.
     int32_t P = 2048;
-    while (P > 256 && wg_cols * ((max_len + P - 1) / P) < 4096) P /= 2;
+    while (P > 256 && wg_cols * ((max_len + P - 1) / P) < 2048) P /= 2;
     if (max_len <= P) P = ((max_len + 63) / 64) * 64;
     return P;
 }
@@ -541,9 +581,12 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
     if ((int64_t)p->kv_heads * (G / pkv::decode_heads_per_wg(G)) > 65535)
         return fail(PKV_ERR_INVALID_ARG, "too many query heads for one launch");
     if (B > 0 && (!q || !out || !block_tables || !context_lens)) return fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+    if (B > 0 && (int64_t)max_blocks_per_seq * B > ((int64_t)1 << 40)) return fail(PKV_ERR_INVALID_ARG, "tables too large");
     if (B > 0 && (!aligned16(q) || !aligned16(out))) return fail(PKV_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
     const int32_t max_len = (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * p->block_size);
     const int32_t P = resolve_partition(p, B, H_q, max_len);
+    if (max_len > 0 && (max_len + (int64_t)P - 1) / P > (1 << 30))
+        return fail(PKV_ERR_INVALID_ARG, "partition of %d tokens is too small for %d tokens", P, max_len);
     size_t ml_bytes = 0;
     const size_t need = workspace_for(p, B, H_q, max_len, P, &ml_bytes);
     if (need > 0 && (!workspace || workspace_bytes < need))

@@ -232,3 +232,46 @@ def test_partition_heuristic_is_multiple_of_64():
         if ml <= P:
             assert p.workspace_bytes(B, Hq, ml) == 0
     p.close()
+
+
+def test_batch_reserve_matches_single_reserves():
+    """kv_batch_reserve == the model's reserves in order; all or nothing when the pool runs out."""
+    import copy
+    rng = np.random.default_rng(5)
+    order = rng.permutation(40)
+    a = pkv.KVPool(40, 2, 16, pkv.F16, free_order=order, host_only=True)
+    m = BlockPoolModel(40, 16, free_order=order)
+    seqs = [a.seq_create() for _ in range(5)]
+    for _ in seqs:
+        m.seq_create()
+    refused = 0
+    for step in range(60):
+        counts = rng.integers(0, 9, size=7)
+        batch = [int(x) for x in rng.choice(seqs, size=7)]      # repeats allowed
+        trial = copy.deepcopy(m)
+        try:
+            want = []
+            for s, k in zip(batch, counts):
+                want += trial.reserve(s, int(k))
+        except AllocError as e:
+            assert e.code == NO_BLOCKS_CODE
+            with pytest.raises(pkv.PagedKVError) as got:
+                a.batch_reserve(batch, counts)
+            assert got.value.code == pkv.ERR_NO_BLOCKS
+            refused += 1
+        else:
+            m = trial
+            assert list(a.batch_reserve(batch, counts)) == want
+        assert list(a.free_list()) == m.free_list()
+        assert [a.seq_length(s) for s in seqs] == [m.length(s) for s in seqs]
+        if step % 10 == 9:                                       # release one to keep going
+            s = seqs.pop(0)
+            a.seq_free(s)
+            m.free_seq(s)
+            seqs.append(a.seq_create())
+            m.seq_create()
+    assert refused > 0
+    a.close()
+
+
+NO_BLOCKS_CODE = 2
