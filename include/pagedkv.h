@@ -234,7 +234,11 @@ int kv_append(kv_pool_t* pool, const int32_t* slot_mapping, int32_t T,
  *   workspace     device scratch of at least paged_decode_workspace_bytes()
  *                 for these B, H_q, max_context_len (NULL allowed if 0).
  * Work is split into partitions of the context; each partition keeps a running
- * max and sum (online softmax) and a second kernel merges partitions.
+ * max and sum (online softmax) and a second kernel merges partitions.  When a
+ * context spans several partitions a small first kernel lists the live
+ * (sequence, partition) items in the workspace, longest first, and the
+ * partition kernel works through that list; the workspace also holds the
+ * partials.  Calls that share one workspace must not overlap on the device.
  * Errors: INVALID_ARG, UNSUPPORTED (no kernel for dtype/head_dim/group: the
  * library refuses rather than fall back), STATE (host-only pool), DEVICE. */
 int paged_decode(kv_pool_t* pool, const void* q, int32_t q_dtype, int32_t B, int32_t H_q,

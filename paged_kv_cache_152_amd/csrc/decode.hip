@@ -26,7 +26,10 @@
 // the V scale multiplies the merged output.
 #include "internal.h"
 
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 namespace pkv {
 namespace {
@@ -241,24 +244,117 @@ __device__ __forceinline__ void ping_pong(int nmine, Fetch&& fetch, Consume&& co
 }
 
 // ---------------------------------------------------------------------------
+// Work distribution.
+//
+// Dense mode (no work list): a grid (partition, head group, sequence), one
+// item per workgroup; used when every context fits one partition.
+//
+// Planned mode: kernel 0 (paged_decode_plan) lists the live (sequence,
+// partition) items longest first, and the partition kernel runs a grid only
+// as large as the GPU holds at once.  Each workgroup takes item blockIdx.x,
+// then further items from an atomic counter, until the list is exhausted:
+// long partitions start first and short ones fill the tail.  Items are
+// expanded over head groups (consecutive virtual items share a partition, so
+// the heads of one block are read close together in time).  Which workgroup
+// computes an item has no influence on the bits it produces.
+// ---------------------------------------------------------------------------
+template <class F>
+__device__ __forceinline__ void for_each_item(const DecodeParams& p, F&& f) {
+    __shared__ int s_next;
+    const bool planned = p.items != nullptr;
+    const int HG = p.head_groups;
+    const int total = planned ? p.sched[1] * HG : 1;
+    int v = planned ? (int)blockIdx.x : 0;
+    while (v < total) {                        // one call site, so the item body is inlined
+        int b, part, hgi;
+        if (planned) {
+            const int2 it = p.items[v / HG];
+            b = it.x;
+            part = it.y;
+            hgi = v % HG;
+        } else {
+            b = blockIdx.z;
+            part = blockIdx.x;
+            hgi = blockIdx.y;
+        }
+        f(b, part, hgi);
+        if (!planned) break;
+        __syncthreads();                       // this item's LDS reads are done
+        if (threadIdx.x == 0) s_next = atomicAdd(&p.sched[0], 1) + (int)gridDim.x;
+        __syncthreads();
+        v = s_next;
+    }
+}
+
+// Kernel 0: the work list.  Items are bucketed by partition length (in blocks),
+// 32 buckets, longest bucket first; a zero-length sequence is one item (its
+// output is zeroed).  sched[0] is the work counter, sched[1] the item count.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 32;
+
+__global__ __launch_bounds__(kPlanThreads) void paged_decode_plan(DecodeParams p) {
+    __shared__ int cnt[kPlanBuckets];
+    __shared__ int off[kPlanBuckets];
+    const int tid = threadIdx.x;
+    if (tid < kPlanBuckets) cnt[tid] = 0;
+    __syncthreads();
+    const int max_blk = p.part_tokens / kBlock + 1;
+    auto classify = [&](int b, int& k) {
+        const int n = clamped_len(p, b);
+        k = max(num_parts(p, n), 1);
+        const int per = ((n + kBlock - 1) / kBlock + k - 1) / k;   // blocks per partition
+        return min(kPlanBuckets - 1, (int)((int64_t)per * kPlanBuckets / (max_blk + 1)));
+    };
+    for (int b = tid; b < p.B; b += kPlanThreads) {
+        int k;
+        const int bk = classify(b, k);
+        atomicAdd(&cnt[bk], k);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = kPlanBuckets - 1; i >= 0; --i) {
+            off[i] = run;
+            run += cnt[i];
+        }
+        p.sched[0] = 0;
+        p.sched[1] = run;
+    }
+    __syncthreads();
+    for (int b = tid; b < p.B; b += kPlanThreads) {
+        int k;
+        const int bk = classify(b, k);
+        const int base = atomicAdd(&off[bk], k);
+        for (int i = 0; i < k; ++i) p.items[base + i] = make_int2(b, i);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Vector variant: any dtype, head_dim 16/64/128, any group size up to 8.
 // ---------------------------------------------------------------------------
+template <int NS, int GS, int D>
+struct StreamSmem {
+    float m[NS][GS];
+    float l[NS][GS];
+    float o[NS][GS][D];
+};
+
+// One work item of the vector variant: partition `part` of sequence b for
+// head group hgi (KV head hgi / subs, query heads hq0 .. hq0 + GS - 1).
 template <int KDT, int QDT, int D, int GS>
-__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(DecodeParams p) {
+__device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part, int hgi,
+                                         StreamSmem<kDecodeWaves * Tile<KDT, D>::RPL, GS, D>& sm) {
     using TL = Tile<KDT, D>;
     using RawT = typename Raw<TL::W>::T;
     constexpr int EPL = TL::EPL, LPR = TL::LPR, RPL = TL::RPL, NLOAD = TL::NLOAD;
     constexpr int NS = kDecodeWaves * RPL;   // softmax streams per workgroup
+    auto& s_m = sm.m;
+    auto& s_l = sm.l;
+    auto& s_o = sm.o;
 
-    __shared__ float s_m[NS][GS];
-    __shared__ float s_l[NS][GS];
-    __shared__ float s_o[NS][GS][D];
-
-    const int part = blockIdx.x;
     const int subs = p.G / GS;
-    const int g = blockIdx.y / subs;
-    const int hq0 = g * p.G + (blockIdx.y % subs) * GS;
-    const int b = blockIdx.z;
+    const int g = hgi / subs;
+    const int hq0 = g * p.G + (hgi % subs) * GS;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int r = lane / LPR, c = lane % LPR;
@@ -390,6 +486,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(Deco
     merge_streams<QDT, D, GS, NS>(p, s_m, s_l, s_o, b, hq0, part, R.nparts == 1, vscale);
 }
 
+template <int KDT, int QDT, int D, int GS>
+__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(DecodeParams p) {
+    __shared__ StreamSmem<kDecodeWaves * Tile<KDT, D>::RPL, GS, D> sm;
+    for_each_item(p, [&](int b, int part, int hgi) { vec_item<KDT, QDT, D, GS>(p, b, part, hgi, sm); });
+}
+
 // ---------------------------------------------------------------------------
 // Grouped-query variant (GS >= 3 query heads per KV head, head_dim 128,
 // 16-bit or FP8 KV): Q.K^T on the matrix cores, P.V on the vector ALUs.
@@ -466,21 +568,19 @@ struct GqaTile {
 };
 
 template <int KDT, int QDT, int GS>
-__global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition_gqa(DecodeParams p) {
+__device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part, int hgi,
+                                         StreamSmem<kDecodeWaves * 4, GS, 128>& sm) {
     constexpr int D = 128, KS = 4, NS = kDecodeWaves * 4;
     using TL = GqaTile<KDT>;
     using KRaw = typename TL::KRaw;
     using MT = typename MfmaIn<QDT>::T;
+    auto& s_m = sm.m;
+    auto& s_l = sm.l;
+    auto& s_o = sm.o;
 
-    __shared__ float s_m[NS][GS];
-    __shared__ float s_l[NS][GS];
-    __shared__ float s_o[NS][GS][D];
-
-    const int part = blockIdx.x;
     const int subs = p.G / GS;
-    const int g = blockIdx.y / subs;
-    const int hq0 = g * p.G + (blockIdx.y % subs) * GS;
-    const int b = blockIdx.z;
+    const int g = hgi / subs;
+    const int hq0 = g * p.G + (hgi % subs) * GS;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int r = lane >> 4, c = lane & 15;      // DPP row; lane within the row
@@ -615,6 +715,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition_gqa(
     float vscale = 1.0f;
     if constexpr (KDT == DT_FP8) vscale = p.v_scale[g];
     merge_streams<QDT, D, GS, NS>(p, s_m, s_l, s_o, b, hq0, part, R.nparts == 1, vscale);
+}
+
+template <int KDT, int QDT, int GS>
+__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void paged_decode_partition_gqa(DecodeParams p) {
+    __shared__ StreamSmem<kDecodeWaves * 4, GS, 128> sm;
+    for_each_item(p, [&](int b, int part, int hgi) { gqa_item<KDT, QDT, GS>(p, b, part, hgi, sm); });
 }
 
 // Wave-wide max / sum; every lane gets the same value (fixed butterfly order).
@@ -795,15 +902,45 @@ bool decode_supported(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G) {
            pick_reduce(q_dt, D) != nullptr;
 }
 
+// Workgroups of `fn` that fit on the device at once (cached per kernel).
+int resident_workgroups(KernelFn fn) {
+    static std::mutex mu;
+    static std::unordered_map<const void*, int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(reinterpret_cast<const void*>(fn));
+    if (it != cache.end()) return it->second;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),
+                                                     kDecodeWaves * 64, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+        return 1024;   // not cached: a later call retries the query
+    cache[reinterpret_cast<const void*>(fn)] = cus * per_cu;
+    return cus * per_cu;
+}
+
+hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream) {
+    DecodeParams arg = p;
+    void* args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void*>(paged_decode_plan), dim3(1), dim3(kPlanThreads), args, 0,
+                           stream);
+}
+
 hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream) {
     const int gs = decode_heads_per_wg(p.G);
     KernelFn fn = pick_partition(p.kv_dt, p.q_dt, p.D, gs);
     if (!fn) return hipErrorInvalidValue;
-    dim3 grid((unsigned)p.max_parts, (unsigned)(p.H_kv * (p.G / gs)), (unsigned)p.B);
+    dim3 grid;
+    if (p.items) {
+        const int64_t upper = (int64_t)p.B * p.max_parts * p.head_groups;
+        grid = dim3((unsigned)std::min<int64_t>(upper, resident_workgroups(fn)));
+    } else {
+        grid = dim3((unsigned)p.max_parts, (unsigned)p.head_groups, (unsigned)p.B);
+    }
     DecodeParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, dim3(kDecodeWaves * 64), args, 0,
-                           stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, dim3(kDecodeWaves * 64), args, 0, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {

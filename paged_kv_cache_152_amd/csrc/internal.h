@@ -40,8 +40,11 @@ struct DecodeParams {
     const int32_t* lens;      // [B]
     float* ws_ml;             // [B][H_q][max_parts][2]  (running max, sum) per partition
     float* ws_o;              // [B][H_q][max_parts][D]  unnormalised partial output
+    int32_t* sched;           // planned mode: [0] work counter, [1] item count
+    int2* items;              // planned mode: (sequence, partition) work list; NULL = dense grid
     int32_t B, H_q, H_kv, G, D, num_blocks, max_blocks, max_len;
     int32_t part_tokens, max_parts;
+    int32_t head_groups;      // H_kv * (G / heads per workgroup)
     int32_t kv_dt, q_dt;
     float scale;              // softmax scale as given
 };
@@ -51,6 +54,7 @@ struct DecodeParams {
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 bool decode_supported(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G);
 int decode_heads_per_wg(int32_t G);
+hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

@@ -521,24 +521,35 @@ int32_t resolve_partition(const kv_pool* p, int32_t B, int32_t H_q, int32_t max_
     if (p->partition_tokens > 0) return p->partition_tokens;
     const int64_t G = H_q / p->kv_heads;
     const int64_t wg_cols = (int64_t)B * p->kv_heads * (G / pkv::decode_heads_per_wg((int32_t)G));
-    // Largest partition in [256, 2048] that still gives >= 2048 workgroups
-    // (8 per CU), so the 256 CUs stay busy without making any one workgroup long
-    // enough to dominate the tail; short contexts take a single partition.
-    int32_t P = 2048;
-    while (P > 256 && wg_cols * ((max_len + P - 1) / P) < 2048) P /= 2;
+    // Largest partition in [256, 4096] that still gives >= 512 work items (two
+    // per CU).  Multi-partition launches are scheduled longest-first from a work
+    // list, so long partitions do not stretch the tail, and fewer partitions
+    // mean less merging; short contexts take a single partition.
+    int32_t P = 4096;
+    while (P > 256 && wg_cols * ((max_len + P - 1) / P) < 512) P /= 2;
     if (max_len <= P) P = ((max_len + 63) / 64) * 64;
     return P;
 }
 
-size_t workspace_for(const kv_pool* p, int32_t B, int32_t H_q, int32_t max_len, int32_t P, size_t* ml_bytes) {
+// Workspace of a launch that spans more than one partition (256-byte aligned
+// sections): [schedule header][work list: B*max_parts (sequence, partition)]
+// [(m, l): B*H_q*max_parts float2][partial outputs: B*H_q*max_parts*D float].
+struct WsLayout {
+    size_t items = 0, ml = 0, o = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout workspace_for(const kv_pool* p, int32_t B, int32_t H_q, int32_t max_len, int32_t P) {
+    WsLayout L;
     const int64_t parts = max_len <= 0 ? 1 : (max_len + P - 1) / P;
-    if (parts <= 1) {
-        if (ml_bytes) *ml_bytes = 0;
-        return 0;
-    }
-    const size_t ml = ((size_t)B * H_q * parts * 2 * sizeof(float) + 255) & ~(size_t)255;
-    if (ml_bytes) *ml_bytes = ml;
-    return ml + (size_t)B * H_q * parts * p->head_dim * sizeof(float);
+    if (parts <= 1 || B <= 0) return L;
+    const size_t slots = (size_t)B * H_q * parts;
+    L.items = 256;
+    L.ml = L.items + align256((size_t)B * parts * 2 * sizeof(int32_t));
+    L.o = L.ml + align256(slots * 2 * sizeof(float));
+    L.total = L.o + slots * p->head_dim * sizeof(float);
+    return L;
 }
 
 }  // namespace
@@ -560,7 +571,8 @@ int32_t paged_decode_partition_tokens(const kv_pool_t* p, int32_t B, int32_t H_q
 
 size_t paged_decode_workspace_bytes(const kv_pool_t* p, int32_t B, int32_t H_q, int32_t max_context_len) {
     if (!p || B <= 0 || H_q <= 0 || H_q % p->kv_heads != 0) return 0;
-    return workspace_for(p, B, H_q, max_context_len, resolve_partition(p, B, H_q, max_context_len), nullptr);
+    const int32_t max_len = max_context_len;
+    return workspace_for(p, B, H_q, max_len, resolve_partition(p, B, H_q, max_len)).total;
 }
 
 int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_t H_q, const int32_t* block_tables,
@@ -587,8 +599,8 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
     const int32_t P = resolve_partition(p, B, H_q, max_len);
     if (max_len > 0 && (max_len + (int64_t)P - 1) / P > (1 << 30))
         return fail(PKV_ERR_INVALID_ARG, "partition of %d tokens is too small for %d tokens", P, max_len);
-    size_t ml_bytes = 0;
-    const size_t need = workspace_for(p, B, H_q, max_len, P, &ml_bytes);
+    const WsLayout ws = workspace_for(p, B, H_q, max_len, P);
+    const size_t need = ws.total;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
     if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -605,8 +617,11 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
     d.out = out;
     d.tables = block_tables;
     d.lens = context_lens;
-    d.ws_ml = need ? reinterpret_cast<float*>(workspace) : nullptr;
-    d.ws_o = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ml_bytes) : nullptr;
+    char* wsb = reinterpret_cast<char*>(workspace);
+    d.sched = need ? reinterpret_cast<int32_t*>(wsb) : nullptr;
+    d.items = need ? reinterpret_cast<int2*>(wsb + ws.items) : nullptr;
+    d.ws_ml = need ? reinterpret_cast<float*>(wsb + ws.ml) : nullptr;
+    d.ws_o = need ? reinterpret_cast<float*>(wsb + ws.o) : nullptr;
     d.B = B;
     d.H_q = H_q;
     d.H_kv = p->kv_heads;
@@ -617,11 +632,17 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
     d.max_len = max_len;
     d.part_tokens = P;
     d.max_parts = max_len <= 0 ? 1 : (max_len + P - 1) / P;
+    d.head_groups = p->kv_heads * (G / pkv::decode_heads_per_wg(G));
     d.kv_dt = p->dtype;
     d.q_dt = q_dtype;
     d.scale = scale;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = timed_launch(p, "paged_decode_partition", s, [&] { return pkv::launch_decode_partition(d, s); });
+    hipError_t e = hipSuccess;
+    if (d.items) {
+        e = timed_launch(p, "paged_decode_plan", s, [&] { return pkv::launch_decode_plan(d, s); });
+        if (e != hipSuccess) return hip_fail(e, "paged_decode_plan launch");
+    }
+    e = timed_launch(p, "paged_decode_partition", s, [&] { return pkv::launch_decode_partition(d, s); });
     if (e != hipSuccess) return hip_fail(e, "paged_decode_partition launch");
     if (d.max_parts > 1) {
         e = timed_launch(p, "paged_decode_reduce", s, [&] { return pkv::launch_decode_reduce(d, s); });
