@@ -225,21 +225,24 @@ __device__ __forceinline__ void zero_output(const DecodeParams& p, int b, int hq
         store_out<QDT>(p.out, ((int64_t)b * p.H_q + hq0) * D + i, 0.0f);
 }
 
-// Walk this wave's blocks j = 0 .. nmine-1 with two buffers: block j+1's loads
-// are in flight while block j is consumed, and no registers are copied.
-// fetch(j, buf) issues the loads; consume(j, buf, masked) uses them.
-template <class Buf, class Fetch, class Consume>
-__device__ __forceinline__ void ping_pong(int nmine, Fetch&& fetch, Consume&& consume) {
-    Buf b0, b1;
-    if (nmine > 0) fetch(0, b0);
-    int j = 0;
-    while (j < nmine) {
-        if (j + 1 < nmine) fetch(j + 1, b1);
-        consume(j, b0);
-        if (++j >= nmine) break;
-        if (j + 1 < nmine) fetch(j + 1, b0);
-        consume(j, b1);
-        ++j;
+// Walk this wave's blocks j = 0 .. nmine-1 through a ring of NB buffers: the
+// loads of blocks j+1 .. j+NB-1 are in flight while block j is consumed, and
+// no registers are copied (the ring position is a compile-time index).
+// fetch(j, buf) issues the loads; consume(j, buf) uses them.
+template <int NB, class Buf, class Fetch, class Consume>
+__device__ __forceinline__ void pipeline(int nmine, Fetch&& fetch, Consume&& consume) {
+    Buf ring[NB];
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k)
+        if (k < nmine) fetch(k, ring[k]);
+    for (int j0 = 0; j0 < nmine; j0 += NB) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int j = j0 + k;
+            if (j >= nmine) return;
+            if (j + NB - 1 < nmine) fetch(j + NB - 1, ring[(k + NB - 1) % NB]);
+            consume(j, ring[k]);
+        }
     }
 }
 
@@ -468,7 +471,7 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
         if (blk * kBlock + kBlock > R.pend) update(std::integral_constant<bool, true>{}, blk, B);
         else update(std::integral_constant<bool, false>{}, blk, B);
     };
-    ping_pong<Buf>(nmine, fetch, consume);
+    pipeline<2, Buf>(nmine, fetch, consume);
 
     const int s = wave * RPL + r;
 #pragma unroll
@@ -554,6 +557,34 @@ __device__ __forceinline__ float row_bcast(float v, int src_lane_in_row) {
         case 5: return __builtin_amdgcn_update_dpp(0.0f, v, 0x155, 0xF, 0xF, false);
         case 6: return __builtin_amdgcn_update_dpp(0.0f, v, 0x156, 0xF, 0xF, false);
         default: return __builtin_amdgcn_update_dpp(0.0f, v, 0x157, 0xF, 0xF, false);
+    }
+}
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));   // round to nearest even
+}
+
+__device__ __forceinline__ uint32_t row_bcast_u32(uint32_t v, int src_lane_in_row) {
+    return __float_as_uint(row_bcast(__uint_as_float(v), src_lane_in_row));
+}
+
+// E4M3 codes of two tokens a, b at the same dims as f16 pairs: out[d] =
+// (a[d], b[d]), d = 0..7 (words hold dims 4j .. 4j+3).  v_perm_b32 takes bytes
+// 0-3 from its second source and 4-7 from its first; the f16 widening is exact.
+__device__ __forceinline__ void fp8_token_pairs(const uint2& a, const uint2& b, uint32_t* out) {
+    const uint32_t wa[2] = {a.x, a.y}, wb[2] = {b.x, b.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t lo = __builtin_amdgcn_perm(wb[j], wa[j], 0x05010400u);   // a0 b0 a1 b1
+        const uint32_t hi = __builtin_amdgcn_perm(wb[j], wa[j], 0x07030602u);   // a2 b2 a3 b3
+        out[4 * j + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+        out[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+        out[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+        out[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
     }
 }
 
@@ -677,19 +708,46 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
                 for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
             }
         }
+        if constexpr (KDT != DT_FP8) {
+            // 16-bit values: widen to fp32, one FMA per (head, dim, token)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float vf[8];
-            widen<KDT, TL::KW>(B.v[i], vf);
-            if (MASKED && tok + i >= R.pend) {
+            for (int i = 0; i < 4; ++i) {
+                float vf[8];
+                widen<KDT, TL::KW>(B.v[i], vf);
+                if (MASKED && tok + i >= R.pend) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vf[e] = 0.0f;   // select, never 0 * garbage
+                    for (int e = 0; e < 8; ++e) vf[e] = 0.0f;   // select, never 0 * garbage
+                }
+#pragma unroll
+                for (int h = 0; h < GS; ++h) {
+                    const float ph = row_bcast(pr[i], h);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+                }
             }
+        } else {
+            // E4M3 values: two tokens per v_dot2_f32_f16.  The codes of tokens
+            // (4r, 4r+1) at one dim are paired with v_perm_b32 and widened exactly
+            // to f16; their weights travel as one f16 pair per head (relative
+            // rounding 2^-11 on a weight, far inside the FP8 tolerance).
+            const uint32_t pp[2] = {pack_f16x2(pr[0], pr[1]), pack_f16x2(pr[2], pr[3])};
 #pragma unroll
-            for (int h = 0; h < GS; ++h) {
-                const float ph = row_bcast(pr[i], h);
+            for (int pi = 0; pi < 2; ++pi) {
+                uint32_t vp[8];
+                fp8_token_pairs(B.v[2 * pi], B.v[2 * pi + 1], vp);
+                if (MASKED) {
+                    const uint32_t keep = (tok + 2 * pi < R.pend ? 0x0000FFFFu : 0u) |
+                                          (tok + 2 * pi + 1 < R.pend ? 0xFFFF0000u : 0u);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+                    for (int e = 0; e < 8; ++e) vp[e] &= keep;       // select, never 0 * garbage
+                }
+#pragma unroll
+                for (int h = 0; h < GS; ++h) {
+                    const f16x2_t wh = __builtin_bit_cast(f16x2_t, row_bcast_u32(pp[pi], h));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[h][e] = __builtin_amdgcn_fdot2(wh, __builtin_bit_cast(f16x2_t, vp[e]), acc[h][e], false);
+                }
             }
         }
     };
@@ -699,7 +757,7 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
         if (blk * kBlock + kBlock > R.pend) update(std::integral_constant<bool, true>{}, blk, B);
         else update(std::integral_constant<bool, false>{}, blk, B);
     };
-    ping_pong<Buf>(nmine, fetch, consume);
+    pipeline<2, Buf>(nmine, fetch, consume);
 
     // Merge the 16 streams (4 waves x 4 rows) of each head through LDS.
     const int srow = wave * 4 + r;
