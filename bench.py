@@ -44,15 +44,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def traffic_for(workload: str, kernel: str):
+def traffic_for(workload: str, kernel: str, partition_tokens: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken on the current kernel sources at the same partition size; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel_hash") != kernel_hash() or t.get("partition_tokens") != partition_tokens:
         return None
     return t.get("bytes_per_launch")
 
@@ -192,7 +192,7 @@ def main():
     part_us = kern.get("paged_decode_partition", {}).get("avg_us")
     red_us = kern.get("paged_decode_reduce", {}).get("avg_us", 0.0)
     achieved = kv_bytes / (part_us * 1e-6) / 1e9 if part_us else None
-    traffic = traffic_for(w.name, "paged_decode_partition")
+    traffic = traffic_for(w.name, "paged_decode_partition", P)
     result = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
