@@ -165,12 +165,28 @@ int kv_batch_reserve(kv_pool_t* pool, const int32_t* seqs, int32_t n, const int3
                      int32_t* slots_out);
 
 /* New sequence sharing the first n_shared_tokens of `parent` by reference:
- * the child's table points at the same n_shared/block_size physical blocks,
- * each of whose refcount is incremented ([cf1] §3.3 shared prefix; [lqnn] §3
- * "prefixes shared by reference").  n_shared_tokens must be a multiple of
- * block_size and <= the parent's length (whole blocks only; a shared block is
- * never written, so no copy is ever needed).  Errors: STATE, INVALID_ARG. */
+ * the child's table points at the same ceil(n_shared/block_size) physical
+ * blocks, each of whose refcount is incremented ([cf1] §3.3: beam-search
+ * branches and parallel samples share the prefix blocks; [lqnn] §3).  Any
+ * length in [0, parent length] is allowed.  When a holder of a shared, partly
+ * filled last block reserves new positions, it first takes a fresh block and
+ * owes the device a copy of the shared one (copy-on-write, [cf1] §3.3); the
+ * copy runs on the stream of the next kv_append / paged_decode /
+ * kv_apply_copies on this pool, before that call's own work.  The K/V of the
+ * shared tokens must therefore have been appended before the fork.
+ * Errors: STATE, INVALID_ARG. */
 int kv_seq_fork(kv_pool_t* pool, int32_t parent, int32_t n_shared_tokens, int32_t* child);
+
+/* Copy-on-write block copies owed to the device, oldest first: src[i] ->
+ * dst[i] (host arrays of capacity cap; *n receives the count).
+ * Errors: OUT_OF_RANGE if cap is too small. */
+int kv_pending_copies(const kv_pool_t* pool, int32_t* src, int32_t* dst, int32_t cap, int32_t* n);
+
+/* Perform the owed copy-on-write block copies now, asynchronously on `stream`
+ * (both pools, all KV heads of each block), and clear the list.  kv_append and
+ * paged_decode do this themselves first; a metadata-only pool just clears the
+ * list.  Errors: DEVICE. */
+int kv_apply_copies(kv_pool_t* pool, void* stream);
 
 /* Release a sequence (see above).  Errors: STATE (unknown or already freed). */
 int kv_seq_free(kv_pool_t* pool, int32_t seq);

@@ -20,8 +20,10 @@ What the pages leave open, and the reading taken here:
   * Free-list order: a FIFO deque seeded from a caller-given order; allocation
     pops the front, release pushes to the back, a sequence's blocks in logical
     order.
-  * Sharing is of whole blocks only: a fork shares the first n/bs blocks and
-    needs n % bs == 0 (partial-block copy-on-write is not modelled).
+  * A fork at any length n shares the first ceil(n / bs) blocks.  Writing into
+    a shared, partly filled last block first takes a fresh block from the free
+    list and records a block copy old -> fresh (copy-on-write, [cf1] §3.3); the
+    old block loses one holder.  The copy block is taken before any new block.
   * Reserve is all-or-nothing: without enough free blocks nothing changes.
   * Slot of logical position p: table[p // bs] * bs + p % bs.
 """
@@ -52,6 +54,7 @@ class BlockPoolModel:
         self.ref = [0] * num_blocks
         self.seqs = {}          # id -> [blocks list, length]
         self.next_id = 0
+        self.pending = []       # copy-on-write block copies (src, dst), oldest first
 
     # -- sequences -------------------------------------------------------
     def seq_create(self) -> int:
@@ -74,11 +77,17 @@ class BlockPoolModel:
         new_len = length + n
         if new_len > INT32_MAX:
             raise AllocError(OUT_OF_RANGE, "sequence length overflow")
+        cow = n > 0 and length % self.bs != 0 and self.ref[blocks[-1]] > 1
         need = -(-new_len // self.bs) - len(blocks)
-        if need > len(self.free):
+        if need + cow > len(self.free):
             raise AllocError(NO_BLOCKS, "not enough free blocks")
-        if n > 0 and length % self.bs != 0 and self.ref[blocks[-1]] != 1:
-            raise AllocError(STATE, "would write into a shared block")
+        if cow:
+            old, fresh = blocks[-1], self.free.popleft()
+            assert self.ref[fresh] == 0
+            self.ref[fresh] = 1
+            self.ref[old] -= 1
+            blocks[-1] = fresh
+            self.pending.append((old, fresh))
         for _ in range(need):
             b = self.free.popleft()
             assert self.ref[b] == 0
@@ -90,9 +99,9 @@ class BlockPoolModel:
 
     def fork(self, parent: int, n_shared: int) -> int:
         p = self._get(parent)
-        if n_shared < 0 or n_shared > p[1] or n_shared % self.bs != 0:
-            raise AllocError(INVALID_ARG, "fork length must be block aligned and <= parent length")
-        shared = p[0][: n_shared // self.bs]
+        if n_shared < 0 or n_shared > p[1]:
+            raise AllocError(INVALID_ARG, "fork length must be in [0, parent length]")
+        shared = p[0][: -(-n_shared // self.bs)]
         for b in shared:
             self.ref[b] += 1
         sid = self.seq_create()
@@ -132,6 +141,11 @@ class BlockPoolModel:
 
     def free_list(self):
         return list(self.free)
+
+    def take_copies(self):
+        """The owed copy-on-write copies, clearing the list (as a device call does)."""
+        out, self.pending = self.pending, []
+        return out
 
     def shared_blocks(self) -> int:
         return sum(1 for r in self.ref if r > 1)

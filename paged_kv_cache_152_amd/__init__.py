@@ -74,6 +74,8 @@ _SIGNATURES = {
     "kv_batch_reserve": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
     "kv_seq_fork": (ctypes.c_int, [_P, _I32, _I32, _PI32]),
     "kv_seq_free": (ctypes.c_int, [_P, _I32]),
+    "kv_pending_copies": (ctypes.c_int, [_P, _P, _P, _I32, _PI32]),
+    "kv_apply_copies": (ctypes.c_int, [_P, _P]),
     "kv_seq_length": (ctypes.c_int, [_P, _I32, _PI32]),
     "kv_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
     "kv_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
@@ -254,6 +256,19 @@ class KVPool:
         child = ctypes.c_int32()
         _check(lib().kv_seq_fork(self.handle, parent, n_shared_tokens, ctypes.byref(child)), "kv_seq_fork")
         return child.value
+
+    def pending_copies(self):
+        """Copy-on-write block copies owed to the device: list of (src, dst)."""
+        n = ctypes.c_int32()
+        cap = self.num_blocks
+        src = np.empty(cap, np.int32)
+        dst = np.empty(cap, np.int32)
+        _check(lib().kv_pending_copies(self.handle, src.ctypes.data_as(_P), dst.ctypes.data_as(_P), cap,
+                                       ctypes.byref(n)), "kv_pending_copies")
+        return list(zip(src[: n.value].tolist(), dst[: n.value].tolist()))
+
+    def apply_copies(self, stream=None) -> None:
+        _check(lib().kv_apply_copies(self.handle, None if self.host_only else _stream(stream)), "kv_apply_copies")
 
     def seq_free(self, seq: int) -> None:
         _check(lib().kv_seq_free(self.handle, seq), "kv_seq_free")

@@ -121,7 +121,31 @@ __global__ __launch_bounds__(256) void pkv_copy_kernel(uint4* __restrict__ dst,
     for (; i < n; i += stride) dst[i] = src[i];
 }
 
+// Copy-on-write: copy whole blocks (all KV heads) src[i] -> dst[i] in both
+// pools; blockIdx.y selects the pair, 16 bytes per thread.
+__global__ __launch_bounds__(256) void kv_copy_blocks(CopyParams p) {
+    const int pair = blockIdx.y;
+    const int64_t n16 = p.block_bytes / 16;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (pair >= p.n || i >= 2 * n16) return;
+    const bool v = i >= n16;
+    const int64_t j = v ? i - n16 : i;
+    char* base = reinterpret_cast<char*>(v ? p.v_pool : p.k_pool);
+    const uint4* src = reinterpret_cast<const uint4*>(base + (int64_t)p.src[pair] * p.block_bytes);
+    uint4* dst = reinterpret_cast<uint4*>(base + (int64_t)p.dst[pair] * p.block_bytes);
+    dst[j] = src[j];
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream) {
+    if (p.n <= 0) return hipSuccess;
+    CopyParams arg = p;
+    void* args[] = {&arg};
+    const int64_t threads = 2 * (p.block_bytes / 16);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kv_copy_blocks),
+                           dim3((unsigned)((threads + 255) / 256), (unsigned)p.n), dim3(256), args, 0, stream);
+}
 
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream) {
     if (p.T <= 0) return hipSuccess;

@@ -29,6 +29,18 @@ struct AppendParams {
     int32_t src_dt, dst_dt;
 };
 
+constexpr int kMaxCopiesPerLaunch = 128;
+
+// Copy-on-write block copies, passed by value (no device list needed).
+struct CopyParams {
+    int32_t src[kMaxCopiesPerLaunch];
+    int32_t dst[kMaxCopiesPerLaunch];
+    int32_t n;
+    void* k_pool;
+    void* v_pool;
+    int64_t block_bytes;      // bytes of one block over all KV heads (one pool)
+};
+
 struct DecodeParams {
     const void* k_pool;
     const void* v_pool;
@@ -58,5 +70,6 @@ hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 
 }  // namespace pkv

@@ -80,6 +80,9 @@ struct kv_pool {
     std::unordered_map<int32_t, Seq> seqs;
     int32_t next_id = 0;
     int32_t shared = 0;        // blocks with refcount >= 2
+    // copy-on-write: (source, destination) block copies owed to the device,
+    // performed by the next kv_append / paged_decode / kv_apply_copies
+    std::vector<std::pair<int32_t, int32_t>> pending;
 
     bool profiling = false;
     std::vector<KernelTimer> timers;
@@ -334,17 +337,30 @@ int kv_seq_reserve(kv_pool_t* p, int32_t seq, int32_t n_tokens, int32_t* slots) 
     const int64_t new_len = (int64_t)s->len + n_tokens;
     if (new_len > std::numeric_limits<int32_t>::max()) return fail(PKV_ERR_OUT_OF_RANGE, "sequence length overflow");
     const int bs = p->block_size;
-    const int64_t need = (new_len + bs - 1) / bs - (int64_t)s->blocks.size();
+    // Writing into a partly filled block that another table also holds: copy it
+    // first (copy-on-write), so the other holders keep their contents.
+    const bool cow = n_tokens > 0 && s->len % bs != 0 && p->ref[s->blocks.back()] > 1;
+    const int64_t need = (new_len + bs - 1) / bs - (int64_t)s->blocks.size() + (cow ? 1 : 0);
     if (need > (int64_t)p->free_list.size())
         return fail(PKV_ERR_NO_BLOCKS, "need %lld blocks, %zu free", (long long)need, p->free_list.size());
-    if (n_tokens > 0 && s->len % bs != 0 && p->ref[s->blocks.back()] != 1)
-        return fail(PKV_ERR_STATE, "would write into a shared block");
     try {
         s->blocks.reserve(s->blocks.size() + (size_t)need);
+        if (cow) p->pending.reserve(p->pending.size() + 1);
     } catch (...) {
         return fail(PKV_ERR_DEVICE, "host allocation failed");
     }
-    for (int64_t i = 0; i < need; ++i) {
+    int64_t taken = 0;
+    if (cow) {
+        const int32_t old = s->blocks.back();
+        const int32_t fresh = p->free_list.front();
+        p->free_list.pop_front();
+        p->ref[fresh] = 1;
+        ref_dec(p, old);                       // stays >= 1: the block was shared
+        s->blocks.back() = fresh;
+        p->pending.emplace_back(old, fresh);
+        ++taken;
+    }
+    for (; taken < need; ++taken) {
         const int32_t b = p->free_list.front();
         p->free_list.pop_front();
         p->ref[b] = 1;
@@ -362,10 +378,14 @@ int kv_batch_reserve(kv_pool_t* p, const int32_t* seqs, int32_t n, const int32_t
     if (n == 0) return ok();
     if (!seqs || !slots) return fail(PKV_ERR_INVALID_ARG, "NULL array");
     const int bs = p->block_size;
-    // Dry run: lengths after each request (sequences may repeat), total blocks needed.
+    // Dry run, replaying kv_seq_reserve's rules: lengths after each request
+    // (sequences may repeat), copy-on-write departures (which lower the shared
+    // block's count for later requests), total blocks needed.
     int64_t need = 0;
     try {
-        std::unordered_map<int32_t, int64_t> len;
+        std::unordered_map<int32_t, int64_t> len;        // sequence -> simulated length
+        std::unordered_map<int32_t, int32_t> left;       // block -> holders that copied away
+        std::unordered_map<int32_t, bool> own_last;      // sequence -> last block is now private
         for (int32_t i = 0; i < n; ++i) {
             const int32_t k = n_tokens ? n_tokens[i] : 1;
             if (k < 0) return fail(PKV_ERR_INVALID_ARG, "n_tokens[%d] < 0", i);
@@ -375,9 +395,18 @@ int kv_batch_reserve(kv_pool_t* p, const int32_t* seqs, int32_t n, const int32_t
             const int64_t cur = it == len.end() ? s->len : it->second;
             const int64_t nxt = cur + k;
             if (nxt > std::numeric_limits<int32_t>::max()) return fail(PKV_ERR_OUT_OF_RANGE, "sequence length overflow");
-            if (k > 0 && cur == s->len && cur % bs != 0 && p->ref[s->blocks.back()] != 1)
-                return fail(PKV_ERR_STATE, "would write into a shared block");
-            need += (nxt + bs - 1) / bs - (cur + bs - 1) / bs;
+            bool& priv = own_last[seqs[i]];
+            if (k > 0 && cur % bs != 0 && !priv) {
+                const int32_t last = s->blocks.back();
+                if (p->ref[last] - left[last] > 1) {
+                    ++need;
+                    ++left[last];
+                    priv = true;
+                }
+            }
+            const int64_t grown = (nxt + bs - 1) / bs - (cur + bs - 1) / bs;
+            if (grown > 0) priv = true;
+            need += grown;
             len[seqs[i]] = nxt;
         }
     } catch (...) {
@@ -399,13 +428,12 @@ int kv_seq_fork(kv_pool_t* p, int32_t parent, int32_t n_shared, int32_t* child) 
     if (!p || !child) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
     Seq* s = find_seq(p, parent);
     if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", parent);
-    if (n_shared < 0 || n_shared > s->len || n_shared % p->block_size != 0)
-        return fail(PKV_ERR_INVALID_ARG, "fork length %d must be a multiple of %d and <= parent length %d", n_shared,
-                    p->block_size, s->len);
+    if (n_shared < 0 || n_shared > s->len)
+        return fail(PKV_ERR_INVALID_ARG, "fork length %d must be in [0, parent length %d]", n_shared, s->len);
     if (p->next_id == std::numeric_limits<int32_t>::max()) return fail(PKV_ERR_OUT_OF_RANGE, "sequence ids exhausted");
     Seq c;
     try {
-        c.blocks.assign(s->blocks.begin(), s->blocks.begin() + n_shared / p->block_size);
+        c.blocks.assign(s->blocks.begin(), s->blocks.begin() + (n_shared + p->block_size - 1) / p->block_size);
         c.len = n_shared;
         const int32_t id = p->next_id;
         p->seqs.emplace(id, std::move(c));
@@ -478,6 +506,55 @@ int kv_free_list(const kv_pool_t* p, int32_t* out, int32_t cap, int32_t* n) {
     return ok();
 }
 
+int kv_pending_copies(const kv_pool_t* p, int32_t* src, int32_t* dst, int32_t cap, int32_t* n) {
+    if (!p || !n) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    *n = (int32_t)p->pending.size();
+    if (cap < *n) return fail(PKV_ERR_OUT_OF_RANGE, "capacity %d < %d pending copies", cap, *n);
+    if (*n > 0 && (!src || !dst)) return fail(PKV_ERR_INVALID_ARG, "NULL array");
+    for (int32_t i = 0; i < *n; ++i) {
+        src[i] = p->pending[i].first;
+        dst[i] = p->pending[i].second;
+    }
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Perform the pending copy-on-write block copies on `stream` (both pools, all
+// heads of each block) and clear the list.  Metadata-only pools just clear it.
+int flush_copies(kv_pool* p, hipStream_t stream) {
+    if (p->pending.empty()) return PKV_OK;
+    if (!p->host_only) {
+        for (size_t i = 0; i < p->pending.size(); i += pkv::kMaxCopiesPerLaunch) {
+            pkv::CopyParams cp{};
+            cp.n = (int32_t)std::min<size_t>(pkv::kMaxCopiesPerLaunch, p->pending.size() - i);
+            for (int32_t j = 0; j < cp.n; ++j) {
+                cp.src[j] = p->pending[i + j].first;
+                cp.dst[j] = p->pending[i + j].second;
+            }
+            cp.k_pool = p->k_pool;
+            cp.v_pool = p->v_pool;
+            cp.block_bytes = (int64_t)p->kv_heads * p->block_bytes;
+            hipError_t e = timed_launch(p, "kv_copy_blocks", stream, [&] { return pkv::launch_copy_blocks(cp, stream); });
+            if (e != hipSuccess) return hip_fail(e, "kv_copy_blocks launch");
+        }
+    }
+    p->pending.clear();
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_apply_copies(kv_pool_t* p, void* stream) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    const int rc = flush_copies(p, reinterpret_cast<hipStream_t>(stream));
+    return rc == PKV_OK ? ok() : rc;
+}
+
 // ---------------------------------------------------------------- device work
 int kv_append(kv_pool_t* p, const int32_t* slot_mapping, int32_t T, const void* k_new, const void* v_new,
               int32_t src_dtype, void* stream) {
@@ -507,6 +584,8 @@ int kv_append(kv_pool_t* p, const int32_t* slot_mapping, int32_t T, const void* 
     a.src_dt = src_dtype;
     a.dst_dt = p->dtype;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int rc = flush_copies(p, s);       // copy-on-write before the new rows land
+    if (rc != PKV_OK) return rc;
     hipError_t e = timed_launch(p, "kv_append", s, [&] { return pkv::launch_kv_append(a, s); });
     if (e != hipSuccess) return hip_fail(e, "kv_append launch");
     return ok();
@@ -640,6 +719,8 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
     d.q_dt = q_dtype;
     d.scale = scale;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int rc = flush_copies(p, s);       // tables may point at copied blocks
+    if (rc != PKV_OK) return rc;
     hipError_t e = hipSuccess;
     if (d.items) {
         e = timed_launch(p, "paged_decode_plan", s, [&] { return pkv::launch_decode_plan(d, s); });
@@ -657,6 +738,8 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
 int kv_pool_copy_to_host(const kv_pool_t* p, void* k_dst, void* v_dst) {
     if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
     if (p->host_only) return fail(PKV_ERR_STATE, "host-only pool has no device memory");
+    const int rc = flush_copies(const_cast<kv_pool*>(p), nullptr);
+    if (rc != PKV_OK) return rc;
     hipError_t e = hipDeviceSynchronize();
     if (e == hipSuccess && k_dst) e = hipMemcpy(k_dst, p->k_pool, p->pool_bytes, hipMemcpyDeviceToHost);
     if (e == hipSuccess && v_dst) e = hipMemcpy(v_dst, p->v_pool, p->pool_bytes, hipMemcpyDeviceToHost);

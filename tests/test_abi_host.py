@@ -99,7 +99,7 @@ def test_allocator_matches_model_on_random_traces(seed):
             assert pool.seq_length(s) == model.length(s)
         elif op == 3:
             p = live[int(rng.integers(len(live)))]
-            k = 16 * int(rng.integers(0, model.length(p) // 16 + 1))
+            k = int(rng.integers(0, model.length(p) + 1))      # any length: partial blocks shared
             a, b = pool.seq_fork(p, k), model.fork(p, k)
             assert a == b
             live.append(a)
@@ -110,7 +110,11 @@ def test_allocator_matches_model_on_random_traces(seed):
         model.check_invariants()
         if step % 25 == 0:
             _compare(pool, model, live)
+            assert pool.pending_copies() == model.take_copies()
+            pool.apply_copies()
+            assert pool.pending_copies() == []
     _compare(pool, model, live)
+    assert pool.pending_copies() == model.take_copies()
     pool.close()
 
 
@@ -124,7 +128,7 @@ def test_allocator_errors():
     assert e.value.code == pkv.ERR_NO_BLOCKS
     after = (pool.block_tables([s], 4), list(pool.free_list()))
     assert np.array_equal(before[0][0], after[0][0]) and before[1] == after[1]
-    for bad in (20, 48, -16):
+    for bad in (48, -16):
         with pytest.raises(pkv.PagedKVError) as e:
             pool.seq_fork(s, bad)
         assert e.value.code == pkv.ERR_INVALID_ARG
@@ -244,6 +248,12 @@ def test_batch_reserve_matches_single_reserves():
     seqs = [a.seq_create() for _ in range(5)]
     for _ in seqs:
         m.seq_create()
+    # two forks at partial-block lengths, so batches exercise copy-on-write
+    a.seq_reserve(seqs[0], 21)
+    m.reserve(seqs[0], 21)
+    for _ in range(2):
+        seqs.append(a.seq_fork(seqs[0], 21))
+        m.fork(seqs[0], 21)
     refused = 0
     for step in range(60):
         counts = rng.integers(0, 9, size=7)
@@ -264,6 +274,7 @@ def test_batch_reserve_matches_single_reserves():
             assert list(a.batch_reserve(batch, counts)) == want
         assert list(a.free_list()) == m.free_list()
         assert [a.seq_length(s) for s in seqs] == [m.length(s) for s in seqs]
+        assert a.pending_copies() == m.pending
         if step % 10 == 9:                                       # release one to keep going
             s = seqs.pop(0)
             a.seq_free(s)

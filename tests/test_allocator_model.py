@@ -70,9 +70,6 @@ def test_errors_and_atomic_reserve():
     assert e.value.code == NO_BLOCKS
     assert (m.table(s), m.length(s), m.free_list()) == before
     with pytest.raises(AllocError) as e:
-        m.fork(s, 20)
-    assert e.value.code == INVALID_ARG
-    with pytest.raises(AllocError) as e:
         m.fork(s, 48)
     assert e.value.code == INVALID_ARG
     with pytest.raises(AllocError) as e:
@@ -102,9 +99,46 @@ def test_random_traces_keep_invariants():
                     m.reserve(live[rng.integers(len(live))], int(rng.integers(0, 40)))
                 elif op == 2:
                     p = live[rng.integers(len(live))]
-                    live.append(m.fork(p, 16 * int(rng.integers(0, m.length(p) // 16 + 1))))
+                    live.append(m.fork(p, int(rng.integers(0, m.length(p) + 1))))
                 else:
                     m.free_seq(live.pop(rng.integers(len(live))))
             except AllocError as e:
                 assert e.code == NO_BLOCKS
             m.check_invariants()
+
+
+def test_copy_on_write_of_a_shared_partial_block():
+    # cf-1.com/news/5824798 §3.3: branches share the prefix blocks; the first to
+    # write into a shared block gets a copy of it and writes there
+    m = BlockPoolModel(10, 16, free_order=range(10))
+    parent = m.seq_create()
+    m.reserve(parent, 37)                             # blocks 0, 1, 2 (block 2 holds 5 tokens)
+    beams = [m.fork(parent, 37) for _ in range(2)]
+    assert all(m.table(b) == [0, 1, 2] for b in beams) and m.refcount(2) == 3
+    slot = m.reserve(beams[0], 1)                     # writes position 37 -> copy of block 2
+    assert m.table(beams[0]) == [0, 1, 3] and slot == [3 * 16 + 5]
+    assert m.take_copies() == [(2, 3)] and m.refcount(2) == 2
+    slot = m.reserve(parent, 12)                      # positions 37..48: copy, then one new block
+    assert m.table(parent) == [0, 1, 4, 5] and m.take_copies() == [(2, 4)]
+    assert slot[:11] == [4 * 16 + 5 + i for i in range(11)] and slot[11] == 5 * 16
+    assert m.refcount(2) == 1                         # only beams[1] still holds block 2
+    m.reserve(beams[1], 1)                            # sole holder now: writes in place
+    assert m.table(beams[1]) == [0, 1, 2] and m.take_copies() == []
+    # full blocks stay shared, aligned forks never copy
+    assert m.refcount(0) == 3 and m.refcount(1) == 3
+    c = m.fork(parent, 32)
+    m.reserve(c, 3)
+    assert m.table(c)[:2] == [0, 1] and m.take_copies() == []
+    m.check_invariants()
+
+
+def test_copy_on_write_counts_toward_atomic_reserve():
+    m = BlockPoolModel(3, 16)
+    p = m.seq_create()
+    m.reserve(p, 20)                                  # 2 blocks, 1 free
+    c = m.fork(p, 20)
+    m.reserve(c, 1)                                   # copy takes the last free block
+    assert m.free_list() == [] and m.take_copies() == [(1, 2)]
+    with pytest.raises(AllocError) as e:
+        m.reserve(p, 13)                              # sole holder of block 1 now; needs 1 new block
+    assert e.value.code == NO_BLOCKS

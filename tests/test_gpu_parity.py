@@ -398,3 +398,40 @@ def test_full_size_config_sampled(name):
     want = expected(w, seqs=seqs)
     err = assert_close(got[seqs], want, w.kv_dtype, name)
     say(f"{name}: sampled {seqs} max err {err:.2e}")
+
+
+def test_copy_on_write_branches_decode_their_own_history():
+    """Beam-style forks at a partial block (cf-1.com/news/5824798 §3.3): every branch
+    appends its own tokens; each must attend to the shared prompt plus its own tail,
+    the shared full blocks stay shared, and no branch sees another's writes."""
+    rng = np.random.default_rng(17)
+    H_kv, G, D, n0 = 2, 3, 128, 37
+    pool = pkv.KVPool(24, H_kv, D, pkv.F16, free_order=rng.permutation(24))
+    parent = pool.seq_create()
+    K0 = rng.standard_normal((n0, H_kv, D)).astype(np.float16)
+    V0 = rng.standard_normal((n0, H_kv, D)).astype(np.float16)
+    pool.append(torch.from_numpy(pool.seq_reserve(parent, n0)).cuda(), dev(K0, wl.F16), dev(V0, wl.F16))
+    seqs = [parent] + [pool.seq_fork(parent, n0) for _ in range(3)]
+    hist = {s: (K0, V0) for s in seqs}
+    shared_full = pool.block_tables([parent], 8)[0][0][:2].copy()
+    for step in range(20):
+        slots = pool.batch_reserve(seqs)
+        if step == 0:
+            assert len(pool.pending_copies()) == 3             # three writers copy, the last owns it
+        k = rng.standard_normal((len(seqs), H_kv, D)).astype(np.float16)
+        v = rng.standard_normal((len(seqs), H_kv, D)).astype(np.float16)
+        pool.append(torch.from_numpy(slots).cuda(), dev(k, wl.F16), dev(v, wl.F16))
+        assert pool.pending_copies() == []
+        for i, s in enumerate(seqs):
+            hist[s] = (np.concatenate([hist[s][0], k[i:i + 1]]), np.concatenate([hist[s][1], v[i:i + 1]]))
+        tables, lens = pool.block_tables(seqs, 8)
+        q = rng.standard_normal((len(seqs), G * H_kv, D)).astype(np.float16)
+        out = harness.out_to_f64(pool.decode(dev(q, wl.F16), torch.from_numpy(tables).cuda(),
+                                             torch.from_numpy(lens).cuda(), int(lens.max()), 1 / math.sqrt(D)))
+        for i, s in enumerate(seqs):
+            Kh, Vh = hist[s]
+            want = oracle.decode_attention(q[i:i + 1], wl.F16, Kh, Vh, wl.F16, [0], [len(Kh)], 1 / math.sqrt(D))
+            assert_close(out[i:i + 1], want, wl.F16, f"step {step} branch {i}")
+    for blk in shared_full:
+        assert pool.block_refcount(int(blk)) == len(seqs)
+    pool.close()
