@@ -75,6 +75,8 @@ typedef struct {
     int32_t live_seqs;
     int32_t host_only;         /* 1: metadata-only pool, no device memory */
     int32_t partition_tokens;  /* current paged_decode partition setting (0 = automatic) */
+    int32_t cached_blocks;     /* blocks findable by content key (prefix cache) */
+    int32_t evictable_blocks;  /* cached blocks nobody holds (reusable, evicted oldest first) */
 } kv_pool_info_t;
 
 /* Thread-local message of the last failed call on this thread ("" if none). */
@@ -139,8 +141,9 @@ int kv_pool_set_fp8_scales(kv_pool_t* pool, const float* k_scale, const float* v
  * Free list: FIFO, seeded by initial_free_order.  A sequence takes blocks
  * from the front when a new token position p has p % block_size == 0 (only
  * its last block is ever partly filled).  Releasing a sequence decrements the
- * refcount of each of its blocks in logical order; blocks reaching 0 go to the
- * back of the free list.  Slot of logical position p:
+ * refcount of each of its blocks in reverse logical order (deepest first);
+ * blocks reaching 0 go to the back of the free list, or of the evictable list
+ * when they hold a cached prefix block.  Slot of logical position p:
  *   table[p / block_size] * block_size + p % block_size.
  * ------------------------------------------------------------------------ */
 
@@ -176,6 +179,46 @@ int kv_batch_reserve(kv_pool_t* pool, const int32_t* seqs, int32_t n, const int3
  * shared tokens must therefore have been appended before the fork.
  * Errors: STATE, INVALID_ARG. */
 int kv_seq_fork(kv_pool_t* pool, int32_t parent, int32_t n_shared_tokens, int32_t* child);
+
+/* ---------------------------------------------------------------------------
+ * Prefix cache ([cf1] §3.3: a content hash per KV block lets a new request
+ * whose prompt prefix matches reuse the cached physical blocks and skip their
+ * prefill; [lqnn] §3: model, tokenizer, LoRA, RoPE, tenant and version must be
+ * part of the cache identity, here the caller's namespace `ns`).
+ *
+ * A full block's key chains its predecessor's: key_i = kv_block_hash(key_{i-1},
+ * ns, tokens of block i), key_{-1} = 0.  The pool also keeps each cached
+ * block's 16 token ids and shares a block only on an exact token match, so a
+ * hash collision can never serve wrong content.  A cached block whose last
+ * holder is released is not freed but kept, evictable; blocks are allocated
+ * from the free list first and then by evicting the least recently released
+ * cached block.
+ * ------------------------------------------------------------------------ */
+
+/* Key of one 16-token block: SplitMix64's output function folded over parent,
+ * ns and the 16 token ids (tokens NULL: the key of an empty block). */
+uint64_t kv_block_hash(uint64_t parent, uint64_t ns, const int32_t* tokens);
+
+/* Publish the first floor(n_tokens / 16) full blocks of `seq`, whose token ids
+ * are tokens[0 .. n_tokens) (host), under namespace ns.  Blocks whose content
+ * key is already cached, or that already carry a key, are skipped;
+ * *n_registered (nullable) receives the number newly cached.  The K/V of those
+ * tokens must be (or be about to be) appended by the caller.
+ * Errors: STATE (unknown seq), OUT_OF_RANGE (n_tokens > sequence length). */
+int kv_prefix_register(kv_pool_t* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+                       uint64_t ns, int32_t* n_registered);
+
+/* New sequence starting on the longest cached prefix of tokens[0 .. n_tokens)
+ * (host) under ns, whole blocks only: its table points at those cached blocks
+ * (refcount + 1 each; evictable ones are taken back) and its length is
+ * *n_cached_tokens, a multiple of 16.  The caller reserves and appends the
+ * rest.  Never allocates, so it cannot run out of blocks. */
+int kv_seq_create_cached(kv_pool_t* pool, const int32_t* tokens, int32_t n_tokens, uint64_t ns,
+                         int32_t* seq_id, int32_t* n_cached_tokens);
+
+/* Forget every content key (e.g. on a model or scale change): evictable cached
+ * blocks return to the free list now, held ones when released. */
+int kv_prefix_evict_all(kv_pool_t* pool);
 
 /* Copy-on-write block copies owed to the device, oldest first: src[i] ->
  * dst[i] (host arrays of capacity cap; *n receives the count).

@@ -18,14 +18,22 @@ What the pages fix, and where:
 
 What the pages leave open, and the reading taken here:
   * Free-list order: a FIFO deque seeded from a caller-given order; allocation
-    pops the front, release pushes to the back, a sequence's blocks in logical
-    order.
+    pops the front, release pushes to the back.  A freed sequence releases its
+    blocks deepest first (reverse logical order), so that a cached prefix chain
+    is evicted from its tail and its root stays findable longest.
   * A fork at any length n shares the first ceil(n / bs) blocks.  Writing into
     a shared, partly filled last block first takes a fresh block from the free
     list and records a block copy old -> fresh (copy-on-write, [cf1] §3.3); the
     old block loses one holder.  The copy block is taken before any new block.
   * Reserve is all-or-nothing: without enough free blocks nothing changes.
   * Slot of logical position p: table[p // bs] * bs + p % bs.
+  * Prefix cache ([cf1] §3.3 content hash per block; [lqnn] §3 the cache
+    identity includes the model/tenant namespace): full block i of a prompt
+    has key_i = H(key_{i-1}, ns, its 16 tokens), key_{-1} = 0, with H the
+    SplitMix64 output function folded over parent, namespace and tokens.  A
+    block is shared only on an exact token match.  Cached blocks nobody holds
+    stay findable in an LRU list; allocation takes the free list first, then
+    evicts the least recently released cached block.
 """
 from __future__ import annotations
 
@@ -33,6 +41,23 @@ from collections import deque
 
 OK, INVALID_ARG, NO_BLOCKS, OUT_OF_RANGE, STATE = 0, 1, 2, 3, 4
 INT32_MAX = 2**31 - 1
+MASK64 = (1 << 64) - 1
+
+
+def splitmix64(x: int) -> int:
+    """SplitMix64 (Steele, Lea, Flood; Vigna's reference): advance the state by
+    the golden gamma and return the mixed output."""
+    z = (x + 0x9E3779B97F4A7C15) & MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+    return z ^ (z >> 31)
+
+
+def block_key(parent: int, ns: int, tokens) -> int:
+    h = splitmix64(parent ^ splitmix64(ns & MASK64))
+    for t in tokens:
+        h = splitmix64(h ^ (int(t) & 0xFFFFFFFF))
+    return h
 
 
 class AllocError(Exception):
@@ -55,6 +80,29 @@ class BlockPoolModel:
         self.seqs = {}          # id -> [blocks list, length]
         self.next_id = 0
         self.pending = []       # copy-on-write block copies (src, dst), oldest first
+        self.cache = {}         # content key -> block
+        self.key_of = {}        # cached block -> (key, tokens)
+        self.lru = []           # cached blocks nobody holds, oldest release first
+
+    def _take(self) -> int:
+        if self.free:
+            b = self.free.popleft()
+        else:
+            b = self.lru.pop(0)
+            key, _ = self.key_of.pop(b)
+            del self.cache[key]
+        assert self.ref[b] == 0
+        self.ref[b] = 1
+        return b
+
+    def _release(self, b: int) -> None:
+        if b in self.key_of:
+            self.lru.append(b)
+        else:
+            self.free.append(b)
+
+    def available(self) -> int:
+        return len(self.free) + len(self.lru)
 
     # -- sequences -------------------------------------------------------
     def seq_create(self) -> int:
@@ -79,20 +127,15 @@ class BlockPoolModel:
             raise AllocError(OUT_OF_RANGE, "sequence length overflow")
         cow = n > 0 and length % self.bs != 0 and self.ref[blocks[-1]] > 1
         need = -(-new_len // self.bs) - len(blocks)
-        if need + cow > len(self.free):
+        if need + cow > self.available():
             raise AllocError(NO_BLOCKS, "not enough free blocks")
         if cow:
-            old, fresh = blocks[-1], self.free.popleft()
-            assert self.ref[fresh] == 0
-            self.ref[fresh] = 1
+            old, fresh = blocks[-1], self._take()
             self.ref[old] -= 1
             blocks[-1] = fresh
             self.pending.append((old, fresh))
         for _ in range(need):
-            b = self.free.popleft()
-            assert self.ref[b] == 0
-            self.ref[b] = 1
-            blocks.append(b)
+            blocks.append(self._take())
         slots = [blocks[p // self.bs] * self.bs + p % self.bs for p in range(length, new_len)]
         s[1] = new_len
         return slots
@@ -110,12 +153,53 @@ class BlockPoolModel:
 
     def free_seq(self, sid: int) -> None:
         blocks, _ = self._get(sid)
-        for b in blocks:
+        for b in reversed(blocks):
             self.ref[b] -= 1
             assert self.ref[b] >= 0
             if self.ref[b] == 0:
-                self.free.append(b)
+                self._release(b)
         del self.seqs[sid]
+
+    # -- prefix cache ------------------------------------------------------
+    def prefix_register(self, sid: int, tokens, ns: int = 0) -> int:
+        blocks, length = self._get(sid)
+        if len(tokens) > length:
+            raise AllocError(OUT_OF_RANGE, "more tokens than the sequence holds")
+        key, added = 0, 0
+        for i in range(len(tokens) // self.bs):
+            chunk = [int(t) for t in tokens[i * self.bs:(i + 1) * self.bs]]
+            key = block_key(key, ns, chunk)
+            b = blocks[i]
+            if key in self.cache or b in self.key_of:
+                continue
+            self.cache[key] = b
+            self.key_of[b] = (key, chunk)
+            added += 1
+        return added
+
+    def seq_create_cached(self, tokens, ns: int = 0):
+        key, hits = 0, []
+        for i in range(len(tokens) // self.bs):
+            chunk = [int(t) for t in tokens[i * self.bs:(i + 1) * self.bs]]
+            key = block_key(key, ns, chunk)
+            b = self.cache.get(key)
+            if b is None or self.key_of[b][1] != chunk:
+                break
+            hits.append(b)
+        sid = self.seq_create()
+        for b in hits:
+            if self.ref[b] == 0:
+                self.lru.remove(b)
+            self.ref[b] += 1
+        self.seqs[sid] = [hits, len(hits) * self.bs]
+        return sid, len(hits) * self.bs
+
+    def prefix_evict_all(self) -> None:
+        for b in self.lru:
+            self.free.append(b)
+        self.lru = []
+        self.cache = {}
+        self.key_of = {}
 
     # -- queries -----------------------------------------------------------
     def length(self, sid: int) -> int:
@@ -157,11 +241,14 @@ class BlockPoolModel:
             assert len(blocks) == -(-length // self.bs), "blocks != ceil(len / bs)"
             for b in blocks:
                 holders[b] += 1
-        free_set = set(self.free)
+        free_set, lru_set = set(self.free), set(self.lru)
         assert len(free_set) == len(self.free), "a block is in the free list twice"
+        assert len(lru_set) == len(self.lru) and not (free_set & lru_set)
         for b in range(self.N):
-            if b in free_set:
+            if b in free_set or b in lru_set:
                 assert self.ref[b] == 0 and holders[b] == 0
             else:
                 assert self.ref[b] == holders[b] and self.ref[b] > 0, f"refcount mismatch on {b}"
-        assert len(self.free) + sum(1 for r in self.ref if r > 0) == self.N
+        assert all(b in self.key_of for b in self.lru) and not any(b in self.key_of for b in self.free)
+        assert all(self.cache[k] == b for b, (k, _) in self.key_of.items()) and len(self.cache) == len(self.key_of)
+        assert len(self.free) + len(self.lru) + sum(1 for r in self.ref if r > 0) == self.N

@@ -46,7 +46,8 @@ class PoolInfo(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("elem_bytes", ctypes.c_int32),
                 ("free_blocks", ctypes.c_int32), ("used_blocks", ctypes.c_int32),
                 ("shared_blocks", ctypes.c_int32), ("live_seqs", ctypes.c_int32),
-                ("host_only", ctypes.c_int32), ("partition_tokens", ctypes.c_int32)]
+                ("host_only", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
+                ("cached_blocks", ctypes.c_int32), ("evictable_blocks", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -74,6 +75,10 @@ _SIGNATURES = {
     "kv_batch_reserve": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
     "kv_seq_fork": (ctypes.c_int, [_P, _I32, _I32, _PI32]),
     "kv_seq_free": (ctypes.c_int, [_P, _I32]),
+    "kv_block_hash": (ctypes.c_uint64, [ctypes.c_uint64, ctypes.c_uint64, _P]),
+    "kv_prefix_register": (ctypes.c_int, [_P, _I32, _P, _I32, ctypes.c_uint64, _PI32]),
+    "kv_seq_create_cached": (ctypes.c_int, [_P, _P, _I32, ctypes.c_uint64, _PI32, _PI32]),
+    "kv_prefix_evict_all": (ctypes.c_int, [_P]),
     "kv_pending_copies": (ctypes.c_int, [_P, _P, _P, _I32, _PI32]),
     "kv_apply_copies": (ctypes.c_int, [_P, _P]),
     "kv_seq_length": (ctypes.c_int, [_P, _I32, _PI32]),
@@ -121,6 +126,13 @@ def _check(rc: int, where: str) -> None:
 
 def kv_cache_bytes(layers, kv_heads, head_dim, elem_bytes, tokens=1, seqs=1) -> int:
     return int(lib().kv_cache_bytes(layers, kv_heads, head_dim, elem_bytes, tokens, seqs))
+
+
+def kv_block_hash(parent: int, ns: int, tokens) -> int:
+    t, tp = _np_i32(tokens)
+    if len(t) != BLOCK:
+        raise ValueError("a block has 16 tokens")
+    return int(lib().kv_block_hash(parent, ns, tp))
 
 
 # --------------------------------------------------------------------- torch glue
@@ -256,6 +268,25 @@ class KVPool:
         child = ctypes.c_int32()
         _check(lib().kv_seq_fork(self.handle, parent, n_shared_tokens, ctypes.byref(child)), "kv_seq_fork")
         return child.value
+
+    def prefix_register(self, seq: int, tokens, ns: int = 0) -> int:
+        """kv_prefix_register: publish seq's full blocks holding tokens; returns how many were new."""
+        t, tp = _np_i32(tokens)
+        n = ctypes.c_int32()
+        _check(lib().kv_prefix_register(self.handle, seq, tp if len(t) else None, len(t), ns, ctypes.byref(n)),
+               "kv_prefix_register")
+        return n.value
+
+    def seq_create_cached(self, tokens, ns: int = 0):
+        """kv_seq_create_cached: (seq, cached tokens) starting on the longest cached prefix."""
+        t, tp = _np_i32(tokens)
+        sid, hit = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().kv_seq_create_cached(self.handle, tp if len(t) else None, len(t), ns, ctypes.byref(sid),
+                                          ctypes.byref(hit)), "kv_seq_create_cached")
+        return sid.value, hit.value
+
+    def prefix_evict_all(self) -> None:
+        _check(lib().kv_prefix_evict_all(self.handle), "kv_prefix_evict_all")
 
     def pending_copies(self):
         """Copy-on-write block copies owed to the device: list of (src, dst)."""

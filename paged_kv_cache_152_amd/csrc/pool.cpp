@@ -14,8 +14,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <array>
 #include <deque>
 #include <limits>
+#include <list>
 #include <new>
 #include <string>
 #include <unordered_map>
@@ -84,6 +86,15 @@ struct kv_pool {
     // performed by the next kv_append / paged_decode / kv_apply_copies
     std::vector<std::pair<int32_t, int32_t>> pending;
 
+    // prefix cache: content key -> block, and per cached block its key and
+    // tokens; cached blocks nobody holds wait in `lru` (oldest release first)
+    std::unordered_map<uint64_t, int32_t> cache;
+    std::vector<uint64_t> block_key;
+    std::vector<char> is_cached;
+    std::vector<std::array<int32_t, 16>> block_tokens;
+    std::list<int32_t> lru;
+    std::vector<std::list<int32_t>::iterator> lru_pos;
+
     bool profiling = false;
     std::vector<KernelTimer> timers;
     std::vector<hipEvent_t> spare_events;
@@ -101,6 +112,35 @@ void ref_inc(kv_pool* p, int32_t b) {
 
 void ref_dec(kv_pool* p, int32_t b) {
     if (p->ref[b]-- == 2) --p->shared;
+}
+
+// Blocks a reservation can draw on: uncached free blocks, then cached blocks
+// nobody holds (evicted least recently released first).
+size_t available(const kv_pool* p) { return p->free_list.size() + p->lru.size(); }
+
+int32_t take_block(kv_pool* p) {
+    int32_t b;
+    if (!p->free_list.empty()) {
+        b = p->free_list.front();
+        p->free_list.pop_front();
+    } else {
+        b = p->lru.front();                    // evict: forget its content key
+        p->lru.pop_front();
+        p->cache.erase(p->block_key[b]);
+        p->is_cached[b] = 0;
+    }
+    p->ref[b] = 1;
+    return b;
+}
+
+// A block's last holder let go: cached blocks stay findable until evicted.
+void release_block(kv_pool* p, int32_t b) {
+    if (!p->is_cached.empty() && p->is_cached[b]) {
+        p->lru.push_back(b);
+        p->lru_pos[b] = std::prev(p->lru.end());
+    } else {
+        p->free_list.push_back(b);
+    }
 }
 
 int create_common(int32_t num_blocks, int32_t block_size, int32_t kv_heads, int32_t head_dim,
@@ -286,11 +326,13 @@ int kv_pool_info(const kv_pool_t* p, kv_pool_info_t* out) {
     out->dtype = p->dtype;
     out->elem_bytes = p->elem;
     out->free_blocks = (int32_t)p->free_list.size();
-    out->used_blocks = p->num_blocks - out->free_blocks;
+    out->used_blocks = p->num_blocks - out->free_blocks - (int32_t)p->lru.size();
     out->shared_blocks = p->shared;
     out->live_seqs = (int32_t)p->seqs.size();
     out->host_only = p->host_only ? 1 : 0;
     out->partition_tokens = p->partition_tokens;
+    out->cached_blocks = (int32_t)p->cache.size();
+    out->evictable_blocks = (int32_t)p->lru.size();
     return ok();
 }
 
@@ -341,8 +383,8 @@ int kv_seq_reserve(kv_pool_t* p, int32_t seq, int32_t n_tokens, int32_t* slots) 
     // first (copy-on-write), so the other holders keep their contents.
     const bool cow = n_tokens > 0 && s->len % bs != 0 && p->ref[s->blocks.back()] > 1;
     const int64_t need = (new_len + bs - 1) / bs - (int64_t)s->blocks.size() + (cow ? 1 : 0);
-    if (need > (int64_t)p->free_list.size())
-        return fail(PKV_ERR_NO_BLOCKS, "need %lld blocks, %zu free", (long long)need, p->free_list.size());
+    if (need > (int64_t)available(p))
+        return fail(PKV_ERR_NO_BLOCKS, "need %lld blocks, %zu available", (long long)need, available(p));
     try {
         s->blocks.reserve(s->blocks.size() + (size_t)need);
         if (cow) p->pending.reserve(p->pending.size() + 1);
@@ -352,20 +394,13 @@ int kv_seq_reserve(kv_pool_t* p, int32_t seq, int32_t n_tokens, int32_t* slots) 
     int64_t taken = 0;
     if (cow) {
         const int32_t old = s->blocks.back();
-        const int32_t fresh = p->free_list.front();
-        p->free_list.pop_front();
-        p->ref[fresh] = 1;
+        const int32_t fresh = take_block(p);
         ref_dec(p, old);                       // stays >= 1: the block was shared
         s->blocks.back() = fresh;
         p->pending.emplace_back(old, fresh);
         ++taken;
     }
-    for (; taken < need; ++taken) {
-        const int32_t b = p->free_list.front();
-        p->free_list.pop_front();
-        p->ref[b] = 1;
-        s->blocks.push_back(b);
-    }
+    for (; taken < need; ++taken) s->blocks.push_back(take_block(p));
     for (int64_t pos = s->len, i = 0; pos < new_len; ++pos, ++i)
         slots[i] = s->blocks[pos / bs] * bs + (int32_t)(pos % bs);
     s->len = (int32_t)new_len;
@@ -412,8 +447,8 @@ int kv_batch_reserve(kv_pool_t* p, const int32_t* seqs, int32_t n, const int32_t
     } catch (...) {
         return fail(PKV_ERR_DEVICE, "host allocation failed");
     }
-    if (need > (int64_t)p->free_list.size())
-        return fail(PKV_ERR_NO_BLOCKS, "batch needs %lld blocks, %zu free", (long long)need, p->free_list.size());
+    if (need > (int64_t)available(p))
+        return fail(PKV_ERR_NO_BLOCKS, "batch needs %lld blocks, %zu available", (long long)need, available(p));
     int64_t o = 0;
     for (int32_t i = 0; i < n; ++i) {
         const int32_t k = n_tokens ? n_tokens[i] : 1;
@@ -450,9 +485,11 @@ int kv_seq_free(kv_pool_t* p, int32_t seq) {
     if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
     auto it = p->seqs.find(seq);
     if (it == p->seqs.end()) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
-    for (int32_t b : it->second.blocks) {
-        ref_dec(p, b);
-        if (p->ref[b] == 0) p->free_list.push_back(b);
+    // deepest block first: a cached prefix chain then loses its tail before its root
+    const std::vector<int32_t>& blocks = it->second.blocks;
+    for (auto b = blocks.rbegin(); b != blocks.rend(); ++b) {
+        ref_dec(p, *b);
+        if (p->ref[*b] == 0) release_block(p, *b);
     }
     p->seqs.erase(it);
     return ok();
@@ -503,6 +540,112 @@ int kv_free_list(const kv_pool_t* p, int32_t* out, int32_t cap, int32_t* n) {
     if (*n > 0 && !out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
     int32_t i = 0;
     for (int32_t b : p->free_list) out[i++] = b;
+    return ok();
+}
+
+// ------------------------------------------------------------- prefix cache
+uint64_t kv_block_hash(uint64_t parent, uint64_t ns, const int32_t* tokens) {
+    // SplitMix64's output function (Steele, Lea, Flood 2014), folded over the
+    // parent key, the namespace and the block's 16 tokens.
+    auto mix = [](uint64_t x) {
+        x += 0x9E3779B97F4A7C15ull;
+        x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+        x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+        return x ^ (x >> 31);
+    };
+    uint64_t h = mix(parent ^ mix(ns));
+    if (tokens)
+        for (int i = 0; i < pkv::kBlock; ++i) h = mix(h ^ (uint64_t)(uint32_t)tokens[i]);
+    return h;
+}
+
+int kv_prefix_register(kv_pool_t* p, int32_t seq, const int32_t* tokens, int32_t n_tokens, uint64_t ns,
+                       int32_t* n_registered) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    const Seq* s = find_seq(p, seq);
+    if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
+    if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return fail(PKV_ERR_INVALID_ARG, "bad token array");
+    if (n_tokens > s->len) return fail(PKV_ERR_OUT_OF_RANGE, "%d tokens given, sequence holds %d", n_tokens, s->len);
+    const int bs = p->block_size;
+    const int32_t nfull = n_tokens / bs;
+    int32_t added = 0;
+    try {
+        if (p->is_cached.empty()) {
+            p->is_cached.assign(p->num_blocks, 0);
+            p->block_key.assign(p->num_blocks, 0);
+            p->block_tokens.resize(p->num_blocks);
+            p->lru_pos.resize(p->num_blocks);
+        }
+        uint64_t key = 0;
+        for (int32_t i = 0; i < nfull; ++i) {
+            key = kv_block_hash(key, ns, tokens + (int64_t)i * bs);
+            const int32_t b = s->blocks[i];
+            if (p->cache.count(key) || p->is_cached[b]) continue;   // content already cached, or block keyed
+            p->cache.emplace(key, b);
+            p->is_cached[b] = 1;
+            p->block_key[b] = key;
+            std::copy(tokens + (int64_t)i * bs, tokens + (int64_t)(i + 1) * bs, p->block_tokens[b].begin());
+            ++added;
+        }
+    } catch (...) {
+        return fail(PKV_ERR_DEVICE, "host allocation failed");
+    }
+    if (n_registered) *n_registered = added;
+    return ok();
+}
+
+int kv_seq_create_cached(kv_pool_t* p, const int32_t* tokens, int32_t n_tokens, uint64_t ns, int32_t* seq_id,
+                         int32_t* n_cached_tokens) {
+    if (!p || !seq_id || !n_cached_tokens) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return fail(PKV_ERR_INVALID_ARG, "bad token array");
+    if (p->next_id == std::numeric_limits<int32_t>::max()) return fail(PKV_ERR_OUT_OF_RANGE, "sequence ids exhausted");
+    const int bs = p->block_size;
+    Seq s;
+    try {
+        uint64_t key = 0;
+        for (int32_t i = 0; (int64_t)(i + 1) * bs <= n_tokens; ++i) {
+            key = kv_block_hash(key, ns, tokens + (int64_t)i * bs);
+            auto it = p->cache.find(key);
+            if (it == p->cache.end()) break;
+            const int32_t b = it->second;
+            if (!std::equal(tokens + (int64_t)i * bs, tokens + (int64_t)(i + 1) * bs, p->block_tokens[b].begin()))
+                break;                                               // a key collision: never share it
+            s.blocks.push_back(b);
+        }
+        const int32_t id = p->next_id;
+        p->seqs.emplace(id, Seq{});
+        ++p->next_id;
+        for (int32_t b : s.blocks) {
+            if (p->ref[b] == 0) {                                    // evictable: take it back
+                p->lru.erase(p->lru_pos[b]);
+                p->ref[b] = 1;
+            } else {
+                ref_inc(p, b);
+            }
+        }
+        s.len = (int32_t)s.blocks.size() * bs;
+        *n_cached_tokens = s.len;
+        p->seqs[id] = std::move(s);
+        *seq_id = id;
+    } catch (...) {
+        return fail(PKV_ERR_DEVICE, "host allocation failed");
+    }
+    return ok();
+}
+
+int kv_prefix_evict_all(kv_pool_t* p) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    for (int32_t b : p->lru) {
+        p->cache.erase(p->block_key[b]);
+        p->is_cached[b] = 0;
+        p->free_list.push_back(b);
+    }
+    p->lru.clear();
+    // blocks still held lose their keys now and go to the free list when released
+    for (auto it = p->cache.begin(); it != p->cache.end();) {
+        p->is_cached[it->second] = 0;
+        it = p->cache.erase(it);
+    }
     return ok();
 }
 

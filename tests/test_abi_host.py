@@ -69,6 +69,20 @@ def _compare(pool, model, live):
     assert info["free_blocks"] == len(model.free_list())
     assert info["shared_blocks"] == model.shared_blocks()
     assert info["live_seqs"] == len(live)
+    assert info["cached_blocks"] == len(model.cache) and info["evictable_blocks"] == len(model.lru)
+
+
+_TOKS = {}
+
+
+def _tokens(seq, n):
+    """Deterministic token ids for a sequence's first n positions (few distinct
+    prompts, so prefixes repeat across sequences)."""
+    base = _TOKS.get(seq, [])
+    while len(base) < n:
+        base = base + [(seq % 3) * 1000 + len(base) % 37]
+    _TOKS[seq] = base
+    return base[:n]
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -79,9 +93,27 @@ def test_allocator_matches_model_on_random_traces(seed):
     pool = pkv.KVPool(n, 2, 16, pkv.F32, free_order=order, host_only=True)
     model = BlockPoolModel(n, 16, free_order=order)
     live = []
+    _TOKS.clear()
+    hits = evicted = 0
     for step in range(800):
-        op = int(rng.integers(0, 5))
-        if op == 0 or not live:
+        cached_before = len(model.cache)
+        op = int(rng.integers(0, 8))
+        if op == 5 and live:                            # publish a sequence's blocks
+            s = live[int(rng.integers(len(live)))]
+            toks = _tokens(s, model.length(s))
+            assert pool.prefix_register(s, toks, ns=s % 3) == model.prefix_register(s, toks, ns=s % 3)
+        elif op == 6 and live:                          # a request reusing a cached prefix
+            s = live[int(rng.integers(len(live)))]
+            toks = _tokens(s, model.length(s)) + [7] * int(rng.integers(0, 20))
+            a, b = pool.seq_create_cached(toks, ns=s % 3), model.seq_create_cached(toks, ns=s % 3)
+            assert a == b
+            live.append(a[0])
+            _TOKS[a[0]] = toks[: a[1]]
+            hits += a[1] // 16
+        elif op == 7 and rng.random() < 0.05:
+            pool.prefix_evict_all()
+            model.prefix_evict_all()
+        elif op == 0 or not live:
             a, b = pool.seq_create(), model.seq_create()
             assert a == b
             live.append(a)
@@ -108,6 +140,8 @@ def test_allocator_matches_model_on_random_traces(seed):
             pool.seq_free(s)
             model.free_seq(s)
         model.check_invariants()
+        if op in (1, 2) and len(model.cache) < cached_before:
+            evicted += cached_before - len(model.cache)
         if step % 25 == 0:
             _compare(pool, model, live)
             assert pool.pending_copies() == model.take_copies()
@@ -116,6 +150,8 @@ def test_allocator_matches_model_on_random_traces(seed):
     _compare(pool, model, live)
     assert pool.pending_copies() == model.take_copies()
     pool.close()
+    print(f"seed {seed}: {hits} cached blocks reused, {evicted} evicted by allocation")
+    assert hits > 0
 
 
 def test_allocator_errors():
@@ -286,3 +322,15 @@ def test_batch_reserve_matches_single_reserves():
 
 
 NO_BLOCKS_CODE = 2
+
+
+def test_block_hash_matches_model():
+    from oracle.allocator_model import block_key
+    rng = np.random.default_rng(1)
+    parent = 0
+    for i in range(50):
+        toks = rng.integers(-2**31, 2**31 - 1, size=16)
+        ns = int(rng.integers(0, 2**63))
+        k = pkv.kv_block_hash(parent, ns, toks)
+        assert k == block_key(parent, ns, [int(t) for t in toks])
+        parent = k

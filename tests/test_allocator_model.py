@@ -142,3 +142,51 @@ def test_copy_on_write_counts_toward_atomic_reserve():
     with pytest.raises(AllocError) as e:
         m.reserve(p, 13)                              # sole holder of block 1 now; needs 1 new block
     assert e.value.code == NO_BLOCKS
+
+
+def test_splitmix64_published_outputs():
+    # Vigna's splitmix64.c seeded with 0: the state advances by the golden gamma
+    # before each output; its first outputs are these
+    from oracle.allocator_model import splitmix64
+    gamma = 0x9E3779B97F4A7C15
+    outs = [splitmix64((i * gamma) & ((1 << 64) - 1)) for i in range(4)]
+    assert outs == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F, 0xF88BB8A8724C81EC]
+
+
+def test_prefix_cache_reuses_and_evicts_lru():
+    # cf-1.com/news/5824798 §3.3: a request whose prompt prefix matches reuses the
+    # cached blocks; m.lqnn.cn/news/219451 §3: a different identity must miss
+    m = BlockPoolModel(6, 16, free_order=range(6))
+    prompt = list(range(100, 140))                      # 40 tokens: 2 full blocks + 8
+    a = m.seq_create()
+    m.reserve(a, 40)
+    assert m.prefix_register(a, prompt, ns=7) == 2
+    b, hit = m.seq_create_cached(prompt, ns=7)
+    assert hit == 32 and m.table(b) == [0, 1] and m.refcount(0) == 2
+    c, hit = m.seq_create_cached(prompt, ns=8)          # other namespace: no reuse
+    assert hit == 0
+    d, hit = m.seq_create_cached(prompt[:16] + [0] * 24, ns=7)
+    assert hit == 16 and m.table(d) == [0]              # match stops at the first differing block
+    for s in (a, b, c, d):
+        m.free_seq(s)
+    assert m.free_list() == [3, 4, 5, 2] and m.lru == [1, 0]   # cached blocks wait, LRU order
+    e, hit = m.seq_create_cached(prompt, ns=7)          # evictable blocks are taken back
+    assert hit == 32 and m.lru == [] and m.refcount(0) == 1
+    m.free_seq(e)
+    f = m.seq_create()
+    m.reserve(f, 16 * 5)                                # 4 free blocks, then evict the oldest cached
+    assert m.table(f) == [3, 4, 5, 2, 1] and m.lru == [0]
+    g, hit = m.seq_create_cached(prompt, ns=7)          # block 1's content is gone: the chain stops at 0
+    assert hit == 16
+    m.check_invariants()
+
+
+def test_prefix_cache_never_shares_on_a_hash_match_alone():
+    m = BlockPoolModel(4, 16)
+    a = m.seq_create()
+    m.reserve(a, 16)
+    m.prefix_register(a, list(range(16)))
+    key, _ = m.key_of[m.table(a)[0]]
+    m.key_of[m.table(a)[0]] = (key, [999] * 16)         # plant stored tokens that differ
+    _, hit = m.seq_create_cached(list(range(16)))
+    assert hit == 0

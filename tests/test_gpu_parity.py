@@ -435,3 +435,73 @@ def test_copy_on_write_branches_decode_their_own_history():
     for blk in shared_full:
         assert pool.block_refcount(int(blk)) == len(seqs)
     pool.close()
+
+
+def test_prefix_cache_reuse_decodes_the_cached_prompt():
+    """Prefix caching (cf-1.com/news/5824798 §3.3; m.lqnn.cn/news/219451 §3): a
+    request whose prompt starts like a registered one takes over the cached full
+    blocks and computes K/V only for the rest; its decode must equal the oracle
+    over (cached prefix K/V + its own tail).  Blocks released by every holder stay
+    reusable until allocation evicts them, and an evicted block then holds the
+    new owner's data only."""
+    rng = np.random.default_rng(23)
+    H_kv, G, D, N = 2, 4, 128, 48
+    dt, scale = wl.BF16, 1 / math.sqrt(D)
+    pool = pkv.KVPool(N, H_kv, D, pkv.BF16, free_order=rng.permutation(N))
+
+    def kv(n):
+        return (rng.standard_normal((n, H_kv, D)).astype(np.float32),
+                rng.standard_normal((n, H_kv, D)).astype(np.float32))
+
+    def put(seq, K, V):
+        slots = pool.seq_reserve(seq, len(K))
+        pool.append(torch.from_numpy(slots).cuda(), dev(wl.f32_to_bf16_bits(K), dt), dev(wl.f32_to_bf16_bits(V), dt))
+
+    def check(seqs, hist, what):
+        tables, lens = pool.block_tables(seqs, N)
+        q = wl.f32_to_bf16_bits(rng.standard_normal((len(seqs), G * H_kv, D)).astype(np.float32))
+        out = harness.out_to_f64(pool.decode(dev(q, dt), torch.from_numpy(tables).cuda(),
+                                             torch.from_numpy(lens).cuda(), int(lens.max()), scale))
+        for i, (K, V) in enumerate(hist):
+            assert lens[i] == len(K)
+            Kb, Vb = wl.f32_to_bf16_bits(K), wl.f32_to_bf16_bits(V)
+            want = oracle.decode_attention(q[i:i + 1], dt, Kb, Vb, dt, [0], [len(K)], scale)
+            assert_close(out[i:i + 1], want, dt, f"{what} seq {i}")
+
+    prompt = [int(t) for t in rng.integers(0, 32000, size=300)]   # 18 full blocks + 12 tokens
+    a = pool.seq_create()
+    KA, VA = kv(300)
+    put(a, KA, VA)
+    assert pool.prefix_register(a, prompt, ns=5) == 18
+    # B shares 17 blocks (272 tokens), then diverges
+    b_prompt = prompt[:272] + [int(t) for t in rng.integers(0, 32000, size=40)]
+    b, hit = pool.seq_create_cached(b_prompt, ns=5)
+    assert hit == 272 and pool.block_tables([b], 32)[0][0][:17].tolist() == pool.block_tables([a], 32)[0][0][:17].tolist()
+    assert pool.seq_create_cached(prompt, ns=6)[1] == 0                 # other namespace
+    KB, VB = kv(40)
+    put(b, KB, VB)
+    hist_b = (np.concatenate([KA[:272], KB]), np.concatenate([VA[:272], VB]))
+    check([a, b], [(KA, VA), hist_b], "shared prefix")
+    # A finishes: its keyed block 17 stays evictable, its partial block is freed
+    pool.seq_free(a)
+    info = pool.info()
+    assert info["evictable_blocks"] == 1 and info["cached_blocks"] == 18
+    c, hit = pool.seq_create_cached(prompt + [1, 2, 3], ns=5)
+    assert hit == 288 and pool.info()["evictable_blocks"] == 0
+    KC, VC = kv(15)
+    put(c, KC, VC)
+    hist_c = (np.concatenate([KA[:288], KC]), np.concatenate([VA[:288], VC]))
+    check([b, c], [hist_b, hist_c], "reuse after release")
+    # everyone leaves; a long sequence then needs every block: the cache is evicted
+    pool.seq_free(b)
+    pool.seq_free(c)
+    assert pool.info()["evictable_blocks"] == 18
+    d = pool.seq_create()
+    KD, VD = kv(N * 16)
+    put(d, KD, VD)
+    info = pool.info()
+    assert info["cached_blocks"] == 0 and info["free_blocks"] == 0
+    check([d], [(KD, VD)], "after eviction")
+    pool.seq_free(d)
+    assert pool.seq_create_cached(prompt, ns=5)[1] == 0
+    pool.close()
