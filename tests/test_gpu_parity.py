@@ -218,6 +218,20 @@ def test_decode_small_vs_oracle(case, partition):
     say(f"case {case} dt={dt} G={Hq // Hkv} D={D} P={partition}: max err {err:.2e}")
 
 
+@pytest.mark.parametrize("dt", [wl.F32, wl.F16, wl.BF16, wl.E4M3])
+def test_many_partitions_merge(dt):
+    """Contexts of up to 47 partitions mixed with one-partition rows: the
+    log-sum-exp merge matches the oracle and repeats bit for bit."""
+    D = 16 if dt == wl.F32 else 128
+    w = _small(dt, 16, 4, D, [3000, 64, 1, 2049, 16, 700, 3001, 65], seed=61)
+    prep = harness.prepare(w, partition_tokens=64)
+    prep.append_step()
+    runs = [harness.out_to_f64(prep.decode()) for _ in range(3)]
+    prep.pool.close()
+    assert all(np.array_equal(runs[0], r) for r in runs[1:])
+    assert_close(runs[0], expected(w), dt, "many partitions")
+
+
 def test_brute_force_sweep():
     """Random small shapes across dtypes, groups 1/2/4/5, head dims and edge lengths."""
     rng = np.random.default_rng(2024)
