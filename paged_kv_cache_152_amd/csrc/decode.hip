@@ -150,9 +150,20 @@ __device__ __forceinline__ int clamped_len(const DecodeParams& p, int b) {
     return n > p.max_blocks * kBlock ? p.max_blocks * kBlock : n;
 }
 
-__device__ __forceinline__ int num_parts(const DecodeParams& p, int n) {
-    return (n + p.part_tokens - 1) / p.part_tokens;
+// Schedule header in the workspace.  The work counter, hammered by atomics,
+// has a cache line of its own; the item count and the partition length the
+// plan kernel chose sit on another.
+constexpr int kSchedCounter = 0;
+constexpr int kSchedItems = 32;
+constexpr int kSchedPart = 33;
+
+// Partition length in tokens: the plan kernel's choice in planned mode.  Read
+// once per workgroup.
+__device__ __forceinline__ int part_tokens(const DecodeParams& p) {
+    return p.items ? p.sched[kSchedPart] : p.part_tokens;
 }
+
+__device__ __forceinline__ int num_parts(int P, int n) { return (n + P - 1) / P; }
 
 // The k = ceil(n / P) partitions of a sequence split its blocks evenly:
 // partition i covers blocks [i*nb/k, (i+1)*nb/k), so no partition is a small
@@ -161,10 +172,10 @@ struct Range {
     int n, nparts, blk_first, blk_last, pend;
 };
 
-__device__ __forceinline__ Range partition_range(const DecodeParams& p, int b, int part) {
+__device__ __forceinline__ Range partition_range(const DecodeParams& p, int P, int b, int part) {
     Range R;
     R.n = clamped_len(p, b);
-    R.nparts = num_parts(p, R.n);
+    R.nparts = num_parts(P, R.n);
     const int nb = (R.n + kBlock - 1) / kBlock;
     R.blk_first = (int)((int64_t)part * nb / max(R.nparts, 1));
     R.blk_last = (int)((int64_t)(part + 1) * nb / max(R.nparts, 1));
@@ -266,7 +277,8 @@ __device__ __forceinline__ void for_each_item(const DecodeParams& p, F&& f) {
     __shared__ int s_next;
     const bool planned = p.items != nullptr;
     const int HG = p.head_groups;
-    const int total = planned ? p.sched[1] * HG : 1;
+    const int total = planned ? p.sched[kSchedItems] * HG : 1;
+    const int P = part_tokens(p);
     int v = planned ? (int)blockIdx.x : 0;
     while (v < total) {                        // one call site, so the item body is inlined
         int b, part, hgi;
@@ -280,10 +292,10 @@ __device__ __forceinline__ void for_each_item(const DecodeParams& p, F&& f) {
             part = blockIdx.x;
             hgi = blockIdx.y;
         }
-        f(b, part, hgi);
+        f(b, part, hgi, P);
         if (!planned) break;
         __syncthreads();                       // this item's LDS reads are done
-        if (threadIdx.x == 0) s_next = atomicAdd(&p.sched[0], 1) + (int)gridDim.x;
+        if (threadIdx.x == 0) s_next = atomicAdd(&p.sched[kSchedCounter], 1) + (int)gridDim.x;
         __syncthreads();
         v = s_next;
     }
@@ -291,20 +303,72 @@ __device__ __forceinline__ void for_each_item(const DecodeParams& p, F&& f) {
 
 // Kernel 0: the work list.  Items are bucketed by partition length (in blocks),
 // 32 buckets, longest bucket first; a zero-length sequence is one item (its
-// output is zeroed).  sched[0] is the work counter, sched[1] the item count.
+// output is zeroed).  The header holds the work counter, the item count and
+// the partition length used.
+//
+// The partition length is the host's, except when every context has the same
+// length n: then k equal partitions per context give B * head_groups * k
+// items of one size, and a k that makes that a whole number of rounds of the
+// grid (every workgroup the same number of items, no partly idle last round)
+// is taken: the smallest such k with at least one round, up to max_parts
+// (automatic partition only; a partition the caller set is kept).
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = 32;
 
 __global__ __launch_bounds__(kPlanThreads) void paged_decode_plan(DecodeParams p) {
     __shared__ int cnt[kPlanBuckets];
     __shared__ int off[kPlanBuckets];
+    __shared__ int s_min, s_max, s_P;
     const int tid = threadIdx.x;
+    // each thread's first sequence stays in a register (B <= kPlanThreads needs
+    // no second read of context_lens)
+    const int n0 = tid < p.B ? clamped_len(p, tid) : 0;
+    auto len_of = [&](int b) { return b == tid ? n0 : clamped_len(p, b); };
     if (tid < kPlanBuckets) cnt[tid] = 0;
+    if (tid == 0) {
+        s_min = INT_MAX;
+        s_max = 0;
+    }
     __syncthreads();
-    const int max_blk = p.part_tokens / kBlock + 1;
+    int lo = INT_MAX, hi = 0;
+    for (int b = tid; b < p.B; b += kPlanThreads) {
+        const int n = len_of(b);
+        lo = min(lo, n);
+        hi = max(hi, n);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        lo = min(lo, __shfl_xor(lo, o, 64));
+        hi = max(hi, __shfl_xor(hi, o, 64));
+    }
+    if ((tid & 63) == 0) {
+        atomicMin(&s_min, lo);
+        atomicMax(&s_max, hi);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int P = p.part_tokens;
+        const int n = s_max;
+        if (p.choose_parts && n > 0 && s_min == n) {
+            const int64_t cols = (int64_t)p.B * p.head_groups;
+            const int nb = (n + kBlock - 1) / kBlock;
+            for (int k = 1; k <= p.max_parts && k <= nb; ++k) {
+                const int Pk = (n + k - 1) / k;
+                const int64_t items = cols * num_parts(Pk, n);
+                if (items >= p.grid_wgs && items % p.grid_wgs == 0) {
+                    P = Pk;
+                    break;
+                }
+            }
+        }
+        s_P = P;
+    }
+    __syncthreads();
+    const int P = s_P;
+    const int max_blk = (P + kBlock - 1) / kBlock + 1;
     auto classify = [&](int b, int& k) {
-        const int n = clamped_len(p, b);
-        k = max(num_parts(p, n), 1);
+        const int n = len_of(b);
+        k = max(num_parts(P, n), 1);
         const int per = ((n + kBlock - 1) / kBlock + k - 1) / k;   // blocks per partition
         return min(kPlanBuckets - 1, (int)((int64_t)per * kPlanBuckets / (max_blk + 1)));
     };
@@ -320,8 +384,9 @@ __global__ __launch_bounds__(kPlanThreads) void paged_decode_plan(DecodeParams p
             off[i] = run;
             run += cnt[i];
         }
-        p.sched[0] = 0;
-        p.sched[1] = run;
+        p.sched[kSchedCounter] = 0;
+        p.sched[kSchedItems] = run;
+        p.sched[kSchedPart] = P;
     }
     __syncthreads();
     for (int b = tid; b < p.B; b += kPlanThreads) {
@@ -345,7 +410,7 @@ struct StreamSmem {
 // One work item of the vector variant: partition `part` of sequence b for
 // head group hgi (KV head hgi / subs, query heads hq0 .. hq0 + GS - 1).
 template <int KDT, int QDT, int D, int GS>
-__device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part, int hgi,
+__device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part, int hgi, int P,
                                          StreamSmem<kDecodeWaves * Tile<KDT, D>::RPL, GS, D>& sm) {
     using TL = Tile<KDT, D>;
     using RawT = typename Raw<TL::W>::T;
@@ -362,7 +427,7 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
     const int wave = tid >> 6, lane = tid & 63;
     const int r = lane / LPR, c = lane % LPR;
 
-    const Range R = partition_range(p, b, part);
+    const Range R = partition_range(p, P, b, part);
     if (R.n == 0) {                      // empty context: out = 0, written by partition 0
         if (part == 0) zero_output<QDT, D, GS>(p, b, hq0);
         return;
@@ -492,7 +557,7 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
 template <int KDT, int QDT, int D, int GS>
 __global__ __launch_bounds__(kDecodeWaves * 64) void paged_decode_partition(DecodeParams p) {
     __shared__ StreamSmem<kDecodeWaves * Tile<KDT, D>::RPL, GS, D> sm;
-    for_each_item(p, [&](int b, int part, int hgi) { vec_item<KDT, QDT, D, GS>(p, b, part, hgi, sm); });
+    for_each_item(p, [&](int b, int part, int hgi, int P) { vec_item<KDT, QDT, D, GS>(p, b, part, hgi, P, sm); });
 }
 
 // ---------------------------------------------------------------------------
@@ -599,7 +664,7 @@ struct GqaTile {
 };
 
 template <int KDT, int QDT, int GS>
-__device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part, int hgi,
+__device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part, int hgi, int P,
                                          StreamSmem<kDecodeWaves * 4, GS, 128>& sm) {
     constexpr int D = 128, KS = 4, NS = kDecodeWaves * 4;
     using TL = GqaTile<KDT>;
@@ -616,7 +681,7 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
     const int wave = tid >> 6, lane = tid & 63;
     const int r = lane >> 4, c = lane & 15;      // DPP row; lane within the row
 
-    const Range R = partition_range(p, b, part);
+    const Range R = partition_range(p, P, b, part);
     if (R.n == 0) {
         if (part == 0) zero_output<QDT, D, GS>(p, b, hq0);
         return;
@@ -779,7 +844,7 @@ template <int KDT, int QDT, int GS>
 __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void paged_decode_partition_gqa(DecodeParams p) {
     __shared__ StreamSmem<kDecodeWaves * 4, GS, 128> sm;
-    for_each_item(p, [&](int b, int part, int hgi) { gqa_item<KDT, QDT, GS>(p, b, part, hgi, sm); });
+    for_each_item(p, [&](int b, int part, int hgi, int P) { gqa_item<KDT, QDT, GS>(p, b, part, hgi, P, sm); });
 }
 
 // Wave-wide max / sum; every lane gets the same value (fixed butterfly order).
@@ -809,7 +874,7 @@ template <int QDT, int D>
 __global__ __launch_bounds__(64) void paged_decode_reduce(DecodeParams p) {
     constexpr int DPL = D >= 64 ? D / 64 : 1;      // output dims per lane
     const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const int nparts = num_parts(p, clamped_len(p, b));
+    const int nparts = num_parts(part_tokens(p), clamped_len(p, b));
     if (nparts <= 1) return;
     const int64_t base = ((int64_t)b * p.H_q + hq) * p.max_parts;
     const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + base;
@@ -978,6 +1043,11 @@ int resident_workgroups(KernelFn fn) {
     return cus * per_cu;
 }
 
+int decode_resident_workgroups(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G) {
+    KernelFn fn = pick_partition(kv_dt, q_dt, D, decode_heads_per_wg(G));
+    return fn ? resident_workgroups(fn) : 0;
+}
+
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream) {
     DecodeParams arg = p;
     void* args[] = {&arg};
@@ -991,8 +1061,7 @@ hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream) {
     if (!fn) return hipErrorInvalidValue;
     dim3 grid;
     if (p.items) {
-        const int64_t upper = (int64_t)p.B * p.max_parts * p.head_groups;
-        grid = dim3((unsigned)std::min<int64_t>(upper, resident_workgroups(fn)));
+        grid = dim3((unsigned)p.grid_wgs);
     } else {
         grid = dim3((unsigned)p.max_parts, (unsigned)p.head_groups, (unsigned)p.B);
     }

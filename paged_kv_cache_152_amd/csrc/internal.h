@@ -52,10 +52,14 @@ struct DecodeParams {
     const int32_t* lens;      // [B]
     float* ws_ml;             // [B][H_q][max_parts][2]  (running max, sum) per partition
     float* ws_o;              // [B][H_q][max_parts][D]  unnormalised partial output
-    int32_t* sched;           // planned mode: [0] work counter, [1] item count
+    int32_t* sched;           // planned mode: 256-byte schedule header (work counter, item count,
+                              // partition tokens)
     int2* items;              // planned mode: (sequence, partition) work list; NULL = dense grid
     int32_t B, H_q, H_kv, G, D, num_blocks, max_blocks, max_len;
-    int32_t part_tokens, max_parts;
+    int32_t part_tokens;      // dense mode: the partition; planned mode: the host's choice
+    int32_t max_parts;        // partitions the workspace holds per context
+    int32_t grid_wgs;         // planned mode: workgroups of the partition kernel
+    int32_t choose_parts;     // planned mode: the plan kernel may shorten the partition
     int32_t head_groups;      // H_kv * (G / heads per workgroup)
     int32_t kv_dt, q_dt;
     float scale;              // softmax scale as given
@@ -66,6 +70,9 @@ struct DecodeParams {
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 bool decode_supported(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G);
 int decode_heads_per_wg(int32_t G);
+// Workgroups of the partition kernel for this combination that fit on the
+// current device at once (a nominal 1024 if the device cannot be queried).
+int decode_resident_workgroups(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G);
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);

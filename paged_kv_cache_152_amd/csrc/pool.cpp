@@ -765,9 +765,17 @@ struct WsLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Partitions per context the workspace holds.  With the automatic partition
+// it is twice the host's count, so the plan kernel may pick a shorter
+// partition when every context has the same length.
+int64_t parts_capacity(const kv_pool* p, int32_t max_len, int32_t P) {
+    const int64_t parts = max_len <= 0 ? 1 : (max_len + (int64_t)P - 1) / P;
+    return parts <= 1 || p->partition_tokens > 0 ? parts : 2 * parts;
+}
+
 WsLayout workspace_for(const kv_pool* p, int32_t B, int32_t H_q, int32_t max_len, int32_t P) {
     WsLayout L;
-    const int64_t parts = max_len <= 0 ? 1 : (max_len + P - 1) / P;
+    const int64_t parts = parts_capacity(p, max_len, P);
     if (parts <= 1 || B <= 0) return L;
     const size_t slots = (size_t)B * H_q * parts;
     L.items = 256;
@@ -822,7 +830,7 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
     if (B > 0 && (!aligned16(q) || !aligned16(out))) return fail(PKV_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
     const int32_t max_len = (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * p->block_size);
     const int32_t P = resolve_partition(p, B, H_q, max_len);
-    if (max_len > 0 && (max_len + (int64_t)P - 1) / P > (1 << 30))
+    if (max_len > 0 && (max_len + (int64_t)P - 1) / P > (1 << 29))
         return fail(PKV_ERR_INVALID_ARG, "partition of %d tokens is too small for %d tokens", P, max_len);
     const WsLayout ws = workspace_for(p, B, H_q, max_len, P);
     const size_t need = ws.total;
@@ -856,8 +864,13 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
     d.max_blocks = max_blocks_per_seq;
     d.max_len = max_len;
     d.part_tokens = P;
-    d.max_parts = max_len <= 0 ? 1 : (max_len + P - 1) / P;
+    d.max_parts = (int32_t)parts_capacity(p, max_len, P);
+    d.choose_parts = p->partition_tokens == 0;
     d.head_groups = p->kv_heads * (G / pkv::decode_heads_per_wg(G));
+    if (need) {
+        const int64_t upper = (int64_t)B * d.max_parts * d.head_groups;
+        d.grid_wgs = (int32_t)std::min<int64_t>(upper, pkv::decode_resident_workgroups(p->dtype, q_dtype, p->head_dim, G));
+    }
     d.kv_dt = p->dtype;
     d.q_dt = q_dtype;
     d.scale = scale;

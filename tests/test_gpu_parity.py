@@ -232,6 +232,19 @@ def test_many_partitions_merge(dt):
     assert_close(runs[0], expected(w), dt, "many partitions")
 
 
+@pytest.mark.parametrize("dt", [wl.BF16, wl.E4M3])
+def test_uniform_lengths_automatic_partition(dt):
+    """Every context the same length with the automatic partition: the plan
+    kernel re-cuts the contexts into partitions that fill whole rounds of the
+    grid.  Parity with the oracle, and agreement with a fixed partition."""
+    w = _small(dt, 32, 8, 128, [5000] * 8, seed=71)
+    auto = run_case(w, partition=0)
+    fixed = run_case(w, partition=1024)
+    want = expected(w)
+    assert_close(auto, want, dt, "automatic")
+    assert_close(fixed, want, dt, "fixed 1024")
+
+
 def test_brute_force_sweep():
     """Random small shapes across dtypes, groups 1/2/4/5, head dims and edge lengths."""
     rng = np.random.default_rng(2024)
