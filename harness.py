@@ -119,7 +119,9 @@ def prepare(w: wl.Workload, device="cuda", free_order=None, poison=False, step=0
             vstep[b] = V[n_pre]
     max_blocks = max(1, w.max_blocks_per_seq())
     tables, lens = pool.block_tables(seqs, max_blocks)
-    assert np.array_equal(lens, w.lens), "pool lengths differ from the workload"
+    # one decode step is staged: every context holds its prefill plus that step
+    # (the whole context for single-step workloads)
+    assert np.array_equal(lens, w.step_lens()), "pool lengths differ from the workload"
     return Prepared(w=w, pool=pool, seqs=seqs, q=to_device(w.q(step), w.q_dtype, device),
                     tables=torch.from_numpy(tables).to(device), lens=torch.from_numpy(lens).to(device),
                     step_slots=torch.from_numpy(step_slots).to(device),

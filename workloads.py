@@ -107,9 +107,13 @@ class Workload:
         """dtype of the K/V handed to kv_append (bf16 for an FP8 pool)."""
         return BF16 if self.kv_dtype == E4M3 else self.kv_dtype
 
+    def step_lens(self) -> np.ndarray:
+        """Context lengths during the first decode step (prefill + the new token)."""
+        return np.minimum(self.lens, self.prefill + 1).astype(np.int32)
+
     def kv_bytes_per_step(self) -> int:
-        """Algorithmic K+V bytes one decode step reads: every live element once."""
-        return int(self.lens.astype(np.int64).sum()) * self.H_kv * self.D * 2 * ELEM_BYTES[self.kv_dtype]
+        """Algorithmic K+V bytes the first decode step reads: every live element once."""
+        return int(self.step_lens().astype(np.int64).sum()) * self.H_kv * self.D * 2 * ELEM_BYTES[self.kv_dtype]
 
     def max_len(self) -> int:
         return int(self.lens.max()) if self.B else 0
