@@ -78,6 +78,14 @@ def bind(path: str):
         ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    L.oracle_prefill_attention.restype = ctypes.c_int
+    L.oracle_prefill_attention.argtypes = [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     L.oracle_num_threads.restype = ctypes.c_int
     return L
 
@@ -145,6 +153,45 @@ def decode_attention(q: np.ndarray, q_dtype: int, K: np.ndarray, V: np.ndarray, 
         float(np.float32(scale)), nthreads, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_decode_attention rejected its arguments")
+    return out
+
+
+def prefill_attention(q: np.ndarray, q_dtype: int, q_start, K: np.ndarray, V: np.ndarray, kv_dtype: int,
+                      tok_off, lens, scale: float, *, causal: bool = True,
+                      k_scale=None, v_scale=None, nthreads: int = 0) -> np.ndarray:
+    """fp64 multi-query attention over de-paged K/V (oracle_prefill_attention).
+
+    q: [T][H_q][D] storage of q_dtype, sequence s owning query rows
+    q_start[s] .. q_start[s+1]-1 (its last positions); K, V: [tokens][H_kv][D]
+    storage of kv_dtype, sequence s owning tok_off[s] .. tok_off[s]+lens[s]-1.
+    Returns out [T][H_q][D] float64.
+    """
+    q = np.ascontiguousarray(q, dtype=_NP_STORAGE[q_dtype])
+    K = np.ascontiguousarray(K, dtype=_NP_STORAGE[kv_dtype])
+    V = np.ascontiguousarray(V, dtype=_NP_STORAGE[kv_dtype])
+    T, H_q, D = q.shape
+    assert K.ndim == 3 and K.shape == V.shape and K.shape[2] == D
+    H_kv = K.shape[1]
+    q_start = np.ascontiguousarray(q_start, dtype=np.int64)
+    tok_off = np.ascontiguousarray(tok_off, dtype=np.int64)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    S = len(lens)
+    assert q_start.shape == (S + 1,) and tok_off.shape == (S,) and q_start[S] == T
+    for s in range(S):
+        assert 0 <= tok_off[s] and tok_off[s] + lens[s] <= K.shape[0]
+    ks = vs = None
+    if kv_dtype == E4M3:
+        ks = np.ascontiguousarray(k_scale, dtype=np.float32)
+        vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+        assert ks.shape == (H_kv,) and vs.shape == (H_kv,)
+    out = np.empty((T, H_q, D), dtype=np.float64)
+    rc = lib().oracle_prefill_attention(
+        S, H_q, H_kv, D, _ptr(q), q_dtype, _ptr(q_start), _ptr(K), _ptr(V), kv_dtype,
+        _ptr(tok_off), _ptr(lens),
+        _ptr(ks) if ks is not None else None, _ptr(vs) if vs is not None else None,
+        float(np.float32(scale)), 1 if causal else 0, nthreads, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_prefill_attention rejected its arguments")
     return out
 
 

@@ -225,6 +225,80 @@ int oracle_decode_attention(int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
     return bad ? -1 : 0;
 }
 
+/* ------------------------------------------------------------------------
+ * Multi-query attention over de-paged K/V (a prompt chunk, or a whole
+ * prompt, attending through the cache).
+ *
+ * [mlqm] 三 describes the prefill stage: every prompt token's Q, K and V are
+ * computed at once, all K/V are written to the cache, and the queries attend
+ * in parallel; [mlqm] 七 turns on chunked prefill, where a long prompt goes in
+ * pieces.  Sequence s holds n_s = lens[s] tokens in total (its K/V appended
+ * before the call) and brings q_len_s = q_start[s+1] - q_start[s] query
+ * tokens: the last q_len_s positions.  Query token i of s sits at position
+ * p = n_s - q_len_s + i and reads the positions j it may see:
+ *   causal != 0:  j = 0 .. p      (a chunk of one token is exactly decode)
+ *   causal == 0:  j = 0 .. n_s-1  (every token sees the whole context, as the
+ *                                  prefill listing of [mlqm] 四 computes)
+ *   z_j = scale * <q[t][h], K_s[j][g]>,  out[t][h] = sum_j softmax(z)_j V_s[j][g]
+ * with t = q_start[s] + i and g = floor(h / G).  FP8 values are
+ * decode(code) * scale of their head, as for decode.
+ * ---------------------------------------------------------------------- */
+int oracle_prefill_attention(int32_t S, int32_t H_q, int32_t H_kv, int32_t D,
+                             const void* q, int32_t q_dtype, const int64_t* q_start,
+                             const void* K, const void* V, int32_t kv_dtype,
+                             const int64_t* tok_off, const int32_t* lens,
+                             const float* k_scale, const float* v_scale,
+                             float scale, int32_t causal, int32_t nthreads, double* out) {
+    if (S < 0 || H_q <= 0 || H_kv <= 0 || D <= 0 || H_q % H_kv != 0) return -1;
+    if (kv_dtype == OR_E4M3 && (!k_scale || !v_scale)) return -1;
+    for (int32_t s = 0; s < S; ++s)
+        if (q_start[s + 1] < q_start[s] || q_start[s + 1] - q_start[s] > lens[s]) return -1;
+    const int32_t G = H_q / H_kv;
+    const double sc = (double)scale;
+    const int64_t T = q_start[S];
+    int bad = 0;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) reduction(|| : bad)
+#endif
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t s = 0;                                  /* the sequence of query token t */
+        while (q_start[s + 1] <= t) ++s;
+        const int32_t n = lens[s];
+        const int64_t q_len = q_start[s + 1] - q_start[s];
+        const int64_t p = n - q_len + (t - q_start[s]);
+        const int64_t last = causal ? p : n - 1;        /* newest position this token sees */
+        double* z = (double*)malloc(sizeof(double) * (size_t)(last + 1));
+        if (!z) { bad = 1; continue; }
+        for (int32_t h = 0; h < H_q; ++h) {
+            const int32_t g = h / G;
+            const double ks = (kv_dtype == OR_E4M3) ? (double)k_scale[g] : 1.0;
+            const double vs = (kv_dtype == OR_E4M3) ? (double)v_scale[g] : 1.0;
+            const int64_t qbase = (t * H_q + h) * D;
+            double* o = out + qbase;
+            for (int32_t i = 0; i < D; ++i) o[i] = 0.0;
+            for (int64_t j = 0; j <= last; ++j) {
+                const int64_t kbase = ((tok_off[s] + j) * H_kv + g) * (int64_t)D;
+                double dot = 0.0;
+                for (int32_t i = 0; i < D; ++i)
+                    dot += widen(q, q_dtype, qbase + i) * (widen(K, kv_dtype, kbase + i) * ks);
+                z[j] = sc * dot;
+            }
+            double m = z[0];
+            for (int64_t j = 1; j <= last; ++j) if (z[j] > m) m = z[j];
+            double l = 0.0;
+            for (int64_t j = 0; j <= last; ++j) {
+                const double e = exp(z[j] - m);
+                l += e;
+                const int64_t vbase = ((tok_off[s] + j) * H_kv + g) * (int64_t)D;
+                for (int32_t i = 0; i < D; ++i) o[i] += e * (widen(V, kv_dtype, vbase + i) * vs);
+            }
+            for (int32_t i = 0; i < D; ++i) o[i] /= l;
+        }
+        free(z);
+    }
+    return bad ? -1 : 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

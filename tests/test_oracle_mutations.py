@@ -40,6 +40,14 @@ MUTANTS = {
                          [pins.check_attention_textbook, pins.check_attention_closed_forms]),
     "fp8_key_scale_dropped": ("* (widen(K, kv_dtype, kbase + i) * ks)", "* widen(K, kv_dtype, kbase + i)",
                               [pins.check_fp8_attention_on_dequantised_values]),
+    "prefill_queries_at_the_start": ("const int64_t p = n - q_len + (t - q_start[s]);",
+                                     "const int64_t p = (t - q_start[s]);",
+                                     [pins.check_prefill_vs_library_attention, pins.check_prefill_single_token_is_decode]),
+    "prefill_mask_always_causal": ("const int64_t last = causal ? p : n - 1;", "const int64_t last = p;",
+                                   [pins.check_prefill_vs_library_attention]),
+    "prefill_interleaved_heads": ("const int32_t g = h / G;", "const int32_t g = h % H_kv;",
+                                  [pins.check_prefill_vs_library_attention]),
+    "prefill_scale_dropped": ("z[j] = sc * dot;", "z[j] = dot;", [pins.check_prefill_vs_library_attention]),
     "fp8_value_scale_dropped": ("(widen(V, kv_dtype, vbase + i) * vs)", "widen(V, kv_dtype, vbase + i)",
                                 [pins.check_fp8_attention_on_dequantised_values]),
 }

@@ -318,7 +318,124 @@ def test_fp8_attention_on_dequantised_values():
     check_fp8_attention_on_dequantised_values()
 
 
+# ---------------------------------------------------------------------------
+# Multi-query (prefill / chunked prefill) attention
+# ---------------------------------------------------------------------------
+def _prefill_case(seed, lens, q_lens, H_q, H_kv, D, dtype):
+    rng = np.random.default_rng(seed)
+    q_start = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    tok_off = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    q = wl.cast_to_storage(rng.standard_normal((int(q_start[-1]), H_q, D)).astype(np.float32), dtype)
+    K = wl.cast_to_storage(rng.standard_normal((int(np.sum(lens)), H_kv, D)).astype(np.float32), dtype)
+    V = wl.cast_to_storage(rng.standard_normal((int(np.sum(lens)), H_kv, D)).astype(np.float32), dtype)
+    return q, q_start, K, V, tok_off, np.asarray(lens, np.int32)
+
+
+def _sdpa_reference(q64, q_start, K64, V64, tok_off, lens, scale, causal):
+    """torch's scaled_dot_product_attention in float64, one sequence at a time,
+    KV heads repeated per query group, with an explicit mask: query i of a chunk
+    of q_len at the end of n positions may see j <= n - q_len + i."""
+    H_q, H_kv = q64.shape[1], K64.shape[1]
+    out = np.zeros_like(q64)
+    for s in range(len(lens)):
+        n, a, b = int(lens[s]), int(q_start[s]), int(q_start[s + 1])
+        Q = torch.from_numpy(q64[a:b]).permute(1, 0, 2)                           # [H][L][D]
+        Ks = torch.from_numpy(K64[tok_off[s]:tok_off[s] + n]).permute(1, 0, 2)
+        Vs = torch.from_numpy(V64[tok_off[s]:tok_off[s] + n]).permute(1, 0, 2)
+        Ks = Ks.repeat_interleave(H_q // H_kv, dim=0).contiguous()
+        Vs = Vs.repeat_interleave(H_q // H_kv, dim=0).contiguous()
+        L = b - a
+        mask = torch.ones(L, n, dtype=torch.bool)
+        if causal:
+            mask = torch.arange(n)[None, :] <= (n - L + torch.arange(L))[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            Q, Ks, Vs, attn_mask=mask, scale=float(np.float32(scale)))
+        out[a:b] = o.permute(1, 0, 2).numpy()
+    return out
+
+
+def check_prefill_vs_library_attention():
+    # chunks at the end of a cached context, GQA, causal and unmasked
+    cases = [(31, [12, 40, 5], [12, 9, 1], 8, 2, 16, oracle.F32, 0.25),
+             (32, [64, 33], [17, 33], 6, 3, 32, oracle.BF16, 1 / math.sqrt(32)),
+             (33, [20], [7], 4, 4, 8, oracle.F16, 0.6)]
+    for seed, lens, q_lens, Hq, Hkv, D, dt, scale in cases:
+        q, qs, K, V, off, ln = _prefill_case(seed, lens, q_lens, Hq, Hkv, D, dt)
+        for causal in (True, False):
+            got = oracle.prefill_attention(q, dt, qs, K, V, dt, off, ln, scale, causal=causal)
+            ref = _sdpa_reference(oracle.widen(q, dt), qs, oracle.widen(K, dt), oracle.widen(V, dt),
+                                  off, ln, scale, causal)
+            np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_vs_library_attention():
+    check_prefill_vs_library_attention()
+
+
+def check_prefill_single_token_is_decode():
+    # a chunk of one token at the end of the context is the decode step
+    q, qs, K, V, off, ln = _prefill_case(34, [9, 30, 1], [1, 1, 1], 8, 2, 16, oracle.BF16)
+    pre = oracle.prefill_attention(q, oracle.BF16, qs, K, V, oracle.BF16, off, ln, 0.3)
+    dec = oracle.decode_attention(q, oracle.BF16, K, V, oracle.BF16, off, ln, 0.3)
+    np.testing.assert_allclose(pre, dec, rtol=0, atol=1e-13)
+
+
+def test_prefill_single_token_is_decode():
+    check_prefill_single_token_is_decode()
+
+
+def check_prefill_chunks_compose():
+    # mlqm.cn/news/394450, 七 (chunked prefill): a prompt of 12 tokens processed as
+    # chunks of 5 and 7 gives what one chunk of 12 gives, token for token
+    q, qs, K, V, off, ln = _prefill_case(35, [12], [12], 4, 2, 16, oracle.F32)
+    whole = oracle.prefill_attention(q, oracle.F32, qs, K, V, oracle.F32, off, ln, 0.25)
+    first = oracle.prefill_attention(q[:5], oracle.F32, [0, 5], K[:5], V[:5], oracle.F32, [0], [5], 0.25)
+    second = oracle.prefill_attention(q[5:], oracle.F32, [0, 7], K, V, oracle.F32, [0], [12], 0.25)
+    np.testing.assert_allclose(np.concatenate([first, second]), whole, rtol=0, atol=1e-13)
+    # and each row equals decode with the context that row sees
+    for t in range(12):
+        dec = oracle.decode_attention(q[t:t + 1], oracle.F32, K, V, oracle.F32, [0], [t + 1], 0.25)
+        np.testing.assert_allclose(whole[t], dec[0], rtol=0, atol=1e-13)
+
+
+def test_prefill_chunks_compose():
+    check_prefill_chunks_compose()
+
+
+def check_prefill_fp8_on_dequantised_values():
+    rng = np.random.default_rng(36)
+    lens, q_lens, Hq, Hkv, D = [25, 14], [6, 14], 4, 2, 16
+    qs = np.array([0, 6, 20], np.int64)
+    off = np.array([0, 25], np.int64)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((20, Hq, D)).astype(np.float32))
+    codes_k = rng.integers(0, 256, (39, Hkv, D)).astype(np.uint8)
+    codes_v = rng.integers(0, 256, (39, Hkv, D)).astype(np.uint8)
+    codes_k[(codes_k & 0x7F) == 0x7F] = 0x11
+    codes_v[(codes_v & 0x7F) == 0x7F] = 0x22
+    ks = np.array([0.03, 0.5], np.float32)
+    vs = np.array([0.25, 0.0078125], np.float32)
+    got = oracle.prefill_attention(q, oracle.BF16, qs, codes_k, codes_v, oracle.E4M3, off, lens, 0.25,
+                                   k_scale=ks, v_scale=vs)
+    dec = _torch_e4m3_decode()
+    K64 = dec[codes_k] * ks.astype(np.float64)[None, :, None]
+    V64 = dec[codes_v] * vs.astype(np.float64)[None, :, None]
+    ref = _sdpa_reference(wl.bf16_bits_to_f32(q).astype(np.float64), qs, K64, V64, off, lens, 0.25, True)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_fp8_on_dequantised_values():
+    check_prefill_fp8_on_dequantised_values()
+
+
+def test_prefill_rejects_chunk_longer_than_context():
+    q, qs, K, V, off, ln = _prefill_case(37, [4], [4], 2, 2, 8, oracle.F32)
+    with pytest.raises(ValueError):
+        oracle.prefill_attention(q, oracle.F32, qs, K, V, oracle.F32, off, np.array([3], np.int32), 0.5)
+
+
 ALL_CHECKS = [check_kv_sizes, check_f16_widen, check_bf16_widen, check_e4m3_decode,
               check_e4m3_encode, check_attention_textbook, check_attention_closed_forms,
               check_gqa_equals_repeated_mha, check_cached_decode_equals_recompute,
-              check_fp8_attention_on_dequantised_values]
+              check_fp8_attention_on_dequantised_values, check_prefill_vs_library_attention,
+              check_prefill_single_token_is_decode, check_prefill_chunks_compose,
+              check_prefill_fp8_on_dequantised_values]
