@@ -319,6 +319,37 @@ int paged_decode_set_partition(kv_pool_t* pool, int32_t partition_tokens);
 int32_t paged_decode_partition_tokens(const kv_pool_t* pool, int32_t B, int32_t H_q,
                                       int32_t max_context_len);
 
+/* Multi-query attention through block tables: a chunk of prompt tokens per
+ * sequence attending to the cached context and to itself (the prefill stage of
+ * [mlqm] 三, and chunked prefill of [mlqm] 七, over the paged cache of [cf1]
+ * §3.1).  Sequence s holds n_s = context_lens[s] tokens, the chunk's own K/V
+ * already appended (kv_append), and brings q_len_s = q_start[s+1] - q_start[s]
+ * query tokens: its last q_len_s positions.  Query token i of s, at position
+ * p = n_s - q_len_s + i, attends to the positions
+ *   causal != 0:  0 .. p         (a one-token chunk is the decode step)
+ *   causal == 0:  0 .. n_s - 1   (every token sees the whole context)
+ *   out[t][h] = sum_j softmax_j(scale * <q[t][h], K_s[j][g]>) * V_s[j][g],
+ * t = q_start[s] + i, g = h / G.  FP8 pools: stored values are
+ * decode(code) * scale of their KV head.
+ *   q          device [total_q][H_q][head_dim] of q_dtype (BF16 or F16; the
+ *              pool dtype, or either for an FP8 pool), 16-byte aligned.
+ *   q_start    device [n_seqs + 1] int32, non-decreasing, q_start[0] = 0,
+ *              q_start[n_seqs] = total_q, q_len_s <= n_s.
+ *   block_tables, max_blocks_per_seq, context_lens: as for paged_decode;
+ *              context_lens[s] is clamped to 16 * max_blocks_per_seq.
+ *   max_q_len  host upper bound of q_len_s (sizes the grid).
+ *   out        device [total_q][H_q][head_dim] of q_dtype, 16-byte aligned.
+ * Supported: pool dtype F16, BF16 or FP8_E4M3, head_dim 64 or 128, any group
+ * size.  Q.K^T and P.V run on the matrix cores.  Asynchronous on stream; no
+ * workspace.  Device contents are not validated (q_start out of order or
+ * q_len_s > n_s is undefined).  Errors: INVALID_ARG, UNSUPPORTED (F32 pool,
+ * other head_dim), STATE (host-only pool), DEVICE. */
+int paged_prefill(kv_pool_t* pool, const void* q, int32_t q_dtype, int32_t n_seqs, int32_t H_q,
+                  const int32_t* q_start, int32_t total_q, int32_t max_q_len,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, float scale, int32_t causal,
+                  void* out, void* stream);
+
 /* Synchronous copy of the whole K and V pools to host buffers of pool_bytes
  * each (inspection and tests).  Either pointer may be NULL.
  * Errors: STATE (host-only pool), DEVICE. */

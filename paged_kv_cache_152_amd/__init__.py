@@ -89,6 +89,8 @@ _SIGNATURES = {
     "paged_decode": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, ctypes.c_float,
                                     _P, _P, ctypes.c_size_t, _P]),
     "paged_decode_workspace_bytes": (ctypes.c_size_t, [_P, _I32, _I32, _I32]),
+    "paged_prefill": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I32, _I32, _P, _I32, _P, ctypes.c_float,
+                                     _I32, _P, _P]),
     "paged_decode_set_partition": (ctypes.c_int, [_P, _I32]),
     "paged_decode_partition_tokens": (ctypes.c_int32, [_P, _I32, _I32, _I32]),
     "kv_pool_copy_to_host": (ctypes.c_int, [_P, _P, _P]),
@@ -372,6 +374,29 @@ class KVPool:
         _check(lib().paged_decode(self.handle, qp, dtype_code(q), B, H_q, tp, int(block_tables.shape[1]), lp,
                                   int(max_context_len), float(scale), op, wp, wbytes, _stream(stream)),
                "paged_decode")
+        return out
+
+    def prefill(self, q, q_start, block_tables, context_lens, max_q_len: int, scale: float, causal: bool = True,
+                out=None, stream=None):
+        """paged_prefill: q [total_q][H_q][head_dim], sequence s owning query rows
+        q_start[s] .. q_start[s+1]-1 (its last positions) -> out of the same shape."""
+        torch = _torch()
+        T, H_q, D = (int(x) for x in q.shape)
+        if D != self.head_dim:
+            raise ValueError("q head_dim does not match the pool")
+        if out is None:
+            out = torch.empty_like(q)
+        n = int(context_lens.shape[0])
+        qp = _dev(q, "q")
+        op = _dev(out, "out", dtype=q.dtype, shape=q.shape)
+        sp = _dev(q_start, "q_start", torch.int32, shape=(n + 1,))
+        tp = _dev(block_tables, "block_tables", torch.int32)
+        if block_tables.dim() != 2 or block_tables.shape[0] != n:
+            raise ValueError("block_tables must be [n_seqs][max_blocks]")
+        lp = _dev(context_lens, "context_lens", torch.int32, shape=(n,))
+        _check(lib().paged_prefill(self.handle, qp, dtype_code(q), n, H_q, sp, T, int(max_q_len), tp,
+                                   int(block_tables.shape[1]), lp, float(scale), 1 if causal else 0, op,
+                                   _stream(stream)), "paged_prefill")
         return out
 
     def copy_to_host(self):

@@ -65,6 +65,22 @@ struct DecodeParams {
     float scale;              // softmax scale as given
 };
 
+struct PrefillParams {
+    const void* k_pool;
+    const void* v_pool;
+    const float* k_scale;     // FP8 pools only
+    const float* v_scale;
+    const void* q;            // [total_q][H_q][D]
+    void* out;                // [total_q][H_q][D]
+    const int32_t* q_start;   // [n_seqs + 1]
+    const int32_t* tables;    // [n_seqs][max_blocks]
+    const int32_t* lens;      // [n_seqs] context lengths including the chunk
+    int32_t n_seqs, total_q, H_q, H_kv, G, D, num_blocks, max_blocks;
+    int32_t gs;               // query heads per row group (divides G, at most 16)
+    int32_t kv_dt, q_dt, causal;
+    float scale;
+};
+
 // Launch one kernel each; return hipSuccess or the launch error.
 // Unsupported combinations are filtered on the host before these are called.
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
@@ -78,5 +94,9 @@ hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
+bool prefill_supported(int32_t kv_dt, int32_t q_dt, int32_t D);
+int prefill_heads_per_group(int32_t G);
+int64_t prefill_tiles(int32_t G, int32_t max_q_len);
+hipError_t launch_prefill(const PrefillParams& p, int32_t max_q_len, hipStream_t stream);
 
 }  // namespace pkv

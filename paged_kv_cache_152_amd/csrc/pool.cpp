@@ -891,6 +891,64 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
     return ok();
 }
 
+int paged_prefill(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t n_seqs, int32_t H_q, const int32_t* q_start,
+                  int32_t total_q, int32_t max_q_len, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, float scale, int32_t causal, void* out, void* stream) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    if (n_seqs < 0 || n_seqs > 65535) return fail(PKV_ERR_INVALID_ARG, "n_seqs must be in [0, 65535], got %d", n_seqs);
+    if (H_q <= 0 || H_q % p->kv_heads != 0)
+        return fail(PKV_ERR_INVALID_ARG, "H_q (%d) must be a positive multiple of kv_heads (%d)", H_q, p->kv_heads);
+    if (total_q < 0 || max_q_len < 0) return fail(PKV_ERR_INVALID_ARG, "negative query count");
+    if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0");
+    if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+    if (!dtype_known(q_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown q dtype %d", q_dtype);
+    if (!pkv::prefill_supported(p->dtype, q_dtype, p->head_dim))
+        return fail(PKV_ERR_UNSUPPORTED, "no prefill kernel for pool dtype %d, q dtype %d, head_dim %d", p->dtype,
+                    q_dtype, p->head_dim);
+    const int32_t G = H_q / p->kv_heads;
+    const int32_t gs = pkv::prefill_heads_per_group(G);
+    if ((int64_t)p->kv_heads * (G / gs) > 65535) return fail(PKV_ERR_INVALID_ARG, "too many query heads for one launch");
+    if (pkv::prefill_tiles(G, max_q_len) > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "max_q_len too large");
+    const bool work = n_seqs > 0 && total_q > 0 && max_q_len > 0;
+    if (work && (!q || !out || !q_start || !block_tables || !context_lens))
+        return fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+    if (work && (int64_t)max_blocks_per_seq * n_seqs > ((int64_t)1 << 40))
+        return fail(PKV_ERR_INVALID_ARG, "tables too large");
+    if (work && (!aligned16(q) || !aligned16(out))) return fail(PKV_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
+    if (p->host_only) return fail(PKV_ERR_STATE, "host-only pool has no device memory");
+    if (!work) return ok();
+
+    pkv::PrefillParams d{};
+    d.k_pool = p->k_pool;
+    d.v_pool = p->v_pool;
+    d.k_scale = p->scales;
+    d.v_scale = p->scales ? p->scales + p->kv_heads : nullptr;
+    d.q = q;
+    d.out = out;
+    d.q_start = q_start;
+    d.tables = block_tables;
+    d.lens = context_lens;
+    d.n_seqs = n_seqs;
+    d.total_q = total_q;
+    d.H_q = H_q;
+    d.H_kv = p->kv_heads;
+    d.G = G;
+    d.D = p->head_dim;
+    d.num_blocks = p->num_blocks;
+    d.max_blocks = max_blocks_per_seq;
+    d.gs = gs;
+    d.kv_dt = p->dtype;
+    d.q_dt = q_dtype;
+    d.causal = causal != 0;
+    d.scale = scale;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int rc = flush_copies(p, s);       // tables may point at copied blocks
+    if (rc != PKV_OK) return rc;
+    hipError_t e = timed_launch(p, "paged_prefill", s, [&] { return pkv::launch_prefill(d, max_q_len, s); });
+    if (e != hipSuccess) return hip_fail(e, "paged_prefill launch");
+    return ok();
+}
+
 int kv_pool_copy_to_host(const kv_pool_t* p, void* k_dst, void* v_dst) {
     if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
     if (p->host_only) return fail(PKV_ERR_STATE, "host-only pool has no device memory");

@@ -334,3 +334,31 @@ def test_block_hash_matches_model():
         k = pkv.kv_block_hash(parent, ns, toks)
         assert k == block_key(parent, ns, [int(t) for t in toks])
         parent = k
+
+
+def test_prefill_validates_before_device_work():
+    """paged_prefill on a host-only pool: argument errors first, then STATE."""
+    L = pkv.lib()
+    fake = ctypes.c_void_p(0x10000)
+    p = pkv.KVPool(8, 2, 128, pkv.BF16, host_only=True)
+    h = p.handle
+    pre = lambda **kw: L.paged_prefill(h, kw.get("q", fake), kw.get("qdt", pkv.BF16), kw.get("S", 2), kw.get("H", 8),
+                                       kw.get("qs", fake), kw.get("T", 10), kw.get("mq", 8), kw.get("t", fake),
+                                       kw.get("mb", 4), kw.get("l", fake), kw.get("s", 0.1), kw.get("c", 1),
+                                       kw.get("o", fake), None)
+    assert pre(H=7) == pkv.ERR_INVALID_ARG
+    assert pre(S=-1) == pkv.ERR_INVALID_ARG
+    assert pre(T=-1) == pkv.ERR_INVALID_ARG
+    assert pre(mb=0) == pkv.ERR_INVALID_ARG
+    assert pre(s=float("inf")) == pkv.ERR_INVALID_ARG
+    assert pre(qs=None) == pkv.ERR_INVALID_ARG
+    assert pre(o=ctypes.c_void_p(0x10004)) == pkv.ERR_INVALID_ARG      # misaligned
+    assert pre(qdt=pkv.F16) == pkv.ERR_UNSUPPORTED                    # q must match a bf16 pool
+    assert pre() == pkv.ERR_STATE
+    assert pre(T=0) == pkv.ERR_STATE and pre(S=0) == pkv.ERR_STATE    # as paged_decode: no device
+    p.close()
+    for dt, D in ((pkv.F32, 128), (pkv.BF16, 16)):                    # no prefill kernel for these
+        q = pkv.KVPool(8, 2, D, dt, host_only=True)
+        assert L.paged_prefill(q.handle, fake, dt, 1, 2, fake, 1, 1, fake, 1, fake, 0.1, 1, fake, None) \
+            == pkv.ERR_UNSUPPORTED
+        q.close()
