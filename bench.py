@@ -29,12 +29,16 @@ import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode KV GB/s (% of HBM peak) and decode tokens/s per layer, 1 MI355X"
-KERNEL_SOURCES = ["paged_kv_cache_152_amd/csrc/decode.hip", "paged_kv_cache_152_amd/csrc/append.hip"]
+# sources of each measured kernel (a stored traffic figure is valid while they are unchanged)
+KERNEL_SOURCES = {
+    "paged_decode_partition": ["paged_kv_cache_152_amd/csrc/decode.hip", "paged_kv_cache_152_amd/csrc/append.hip"],
+    "paged_prefill": ["paged_kv_cache_152_amd/csrc/prefill.hip"],
+}
 
 
-def kernel_hash() -> str:
+def kernel_hash(kernel: str = "paged_decode_partition") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -52,7 +56,7 @@ def traffic_for(workload: str, kernel: str, partition_tokens: int):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_hash") != kernel_hash() or t.get("partition_tokens") != partition_tokens:
+    if t.get("kernel_hash") != kernel_hash(kernel) or t.get("partition_tokens") != partition_tokens:
         return None
     return t.get("bytes_per_launch")
 
@@ -141,12 +145,142 @@ def cpu_baseline(w: wl.Workload, budget_s: float = 15.0):
                       f"{done_time:.1f} s of CPU time); KV GB/s at the same algorithmic bytes as value"}
 
 
+PREFILL_METRIC = "paged chunked-prefill attention TFLOP/s (algorithmic, causal), 1 MI355X"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(args):
+    """Multi-query attention over the paged cache: one step = kv_append of every
+    sequence's chunk + paged_prefill of the chunk (queries attend causally to the
+    cached tokens and to the chunk).  value = algorithmic flops / step time."""
+    import torch
+    import harness
+    import paged_kv_cache_152_amd as pkv
+
+    w = wl.make_prefill(args.workload)
+    log(f"[bench] workload {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} D={w.D} "
+        f"cached={w.cached} chunk={w.chunk} blocks={w.num_blocks}")
+    order = np.random.default_rng(w.seed).permutation(w.num_blocks)
+    pool = pkv.KVPool(w.num_blocks, w.H_kv, w.D, w.kv_dtype, free_order=order)
+    if args.partition:
+        pool.set_partition(args.partition)
+    seqs, cs, kc, vc = [], [], [], []
+    for bi in range(w.B):
+        K, V = w.kv(bi)
+        s = pool.seq_create()
+        seqs.append(s)
+        slots = pool.seq_reserve(s, w.n)
+        pool.append(torch.from_numpy(slots[: w.cached]).cuda(), harness.to_device(K[: w.cached], w.kv_dtype),
+                    harness.to_device(V[: w.cached], w.kv_dtype))
+        cs.append(slots[w.cached:])
+        kc.append(K[w.cached:])
+        vc.append(V[w.cached:])
+    slots_d = torch.from_numpy(np.concatenate(cs)).cuda()
+    k_d = harness.to_device(np.concatenate(kc), w.kv_dtype)
+    v_d = harness.to_device(np.concatenate(vc), w.kv_dtype)
+    q = harness.to_device(w.q(), w.kv_dtype)
+    out = torch.empty_like(q)
+    q_start = torch.arange(0, (w.B + 1) * w.chunk, w.chunk, dtype=torch.int32, device="cuda")
+    tables, lens = pool.block_tables(seqs, -(-w.n // wl.BLOCK))
+    tables, lens = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+
+    def step():
+        pool.append(slots_d, k_d, v_d)
+        pool.prefill(q, q_start, tables, lens, w.chunk, w.scale, causal=w.causal, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    pool.profile_enable(True)
+    pool.profile_read()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    stats = pool.profile_read()
+    pool.profile_enable(False)
+    pool.close()
+    kern = {k: {"launches": v["launches"], "avg_us": round(v["total_ms"] / max(1, v["launches"]) * 1e3, 3)}
+            for k, v in stats.items()}
+    flops = w.flops()
+    pre_us = kern["paged_prefill"]["avg_us"]
+    achieved = flops / (pre_us * 1e-6) / 1e12
+    log(f"[bench] {ms_step * 1e3:.1f} us/step, paged_prefill {pre_us:.1f} us = {achieved:.1f} TFLOP/s")
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.DTYPE_NAMES[w.kv_dtype],
+        "data": "synthetic (seeded N(0,1) K/V and q; block tables from a seeded permutation of the pool)",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.H_q, "kv_heads": w.H_kv, "head_dim": w.D,
+                   "block_size": wl.BLOCK, "kv_dtype": wl.DTYPE_NAMES[w.kv_dtype], "cached_tokens": w.cached,
+                   "chunk_tokens": w.chunk, "causal": w.causal, "layers": 1},
+        "flops_per_step": flops,
+        "prefill_tokens_per_s_per_layer": round(w.B * w.chunk / (ms_step * 1e-3), 1),
+        "kernels_us": kern,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_for(w.name, "paged_prefill", 0), "kernel": "paged_prefill",
+                     "algorithmic_flops_per_launch": flops,
+                     "timing": "HIP events around each launch on the library's stream, over a second pass "
+                               "of the same K steps"},
+        "kernel_hash": kernel_hash("paged_prefill"),
+    }
+    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_prefill(w, budget_s: float = 15.0):
+    """The fp64 oracle's prefill attention on a bounded sample: the last 64 query
+    rows of a chunk, per sequence, over 2 sequences per call."""
+    import oracle
+    rows, group = 64, 2
+    Ks, Vs, qs = [], [], []
+    qall = w.q()
+    for bi in range(group):
+        K, V = w.kv(bi)
+        Ks.append(K)
+        Vs.append(V)
+        qs.append(qall[(bi + 1) * w.chunk - rows:(bi + 1) * w.chunk])
+    K, V, q = np.concatenate(Ks), np.concatenate(Vs), np.concatenate(qs)
+    q_start = np.arange(0, (group + 1) * rows, rows, dtype=np.int64)
+    off = np.arange(group, dtype=np.int64) * w.n
+    lens = np.full(group, w.n, np.int32)
+    visible = sum(w.n - rows + i + 1 for i in range(rows)) if w.causal else rows * w.n
+    flops_call = group * w.H_q * visible * 4 * w.D
+    done, calls = 0.0, 0
+    while done < budget_s:
+        t0 = time.perf_counter()
+        oracle.prefill_attention(q, w.kv_dtype, q_start, K, V, w.kv_dtype, off, lens, w.scale, causal=w.causal)
+        done += time.perf_counter() - t0
+        calls += 1
+    return {"value": round(calls * flops_call / done / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle, {calls} calls each attending the last {rows} chunk rows of {group} of the "
+                      f"{w.B} sequences over their {w.n}-token contexts ({done:.1f} s of CPU time); TFLOP/s at "
+                      f"the same algorithmic flops per row as value"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8"])
+    ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8", "prefill8b"])
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -155,6 +289,9 @@ def main():
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(each GPU would own its own pool and sequences); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("prefill"):
+        return bench_prefill(args)
 
     import torch
     import harness

@@ -322,3 +322,76 @@ def mini_model_inputs(seed: int, n_tokens: int, d_model: int = 64):
     Wk = rng.standard_normal((d_model, d_model)) * 0.1
     Wv = rng.standard_normal((d_model, d_model)) * 0.1
     return x, Wq, Wk, Wv
+
+
+# ---------------------------------------------------------------------------
+# Multi-query (chunked prefill) workload
+# ---------------------------------------------------------------------------
+@dataclass
+class PrefillWorkload:
+    """B sequences, each with `cached` tokens already in the cache and a chunk of
+    `chunk` new tokens (their K/V appended, then attended causally).  Values
+    N(0,1) per sequence from child seeds of `seed`; queries from child B."""
+    name: str
+    seed: int
+    B: int
+    H_q: int
+    H_kv: int
+    D: int
+    kv_dtype: int
+    cached: int
+    chunk: int
+    causal: bool = True
+
+    @property
+    def n(self) -> int:
+        return self.cached + self.chunk
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+    @property
+    def num_blocks(self) -> int:
+        return self.B * -(-self.n // BLOCK)
+
+    def _children(self):
+        return np.random.SeedSequence(self.seed).spawn(self.B + 1)
+
+    def kv(self, b: int):
+        """K_b, V_b: [n][H_kv][D] in the pool's storage dtype (bf16 bits, f16)."""
+        import torch
+        g = _torch_gen(self._children()[b])
+        per = self.n * self.H_kv * self.D
+        x = torch.randn(2 * per, generator=g, dtype=torch.float32)
+        K = x[:per].reshape(self.n, self.H_kv, self.D)
+        V = x[per:].reshape(self.n, self.H_kv, self.D)
+        return cast_to_storage(K, self.kv_dtype), cast_to_storage(V, self.kv_dtype)
+
+    def q(self) -> np.ndarray:
+        """[B * chunk][H_q][D], sequence b owning rows b*chunk .. (b+1)*chunk - 1."""
+        import torch
+        x = torch.randn(self.B * self.chunk * self.H_q * self.D, generator=_torch_gen(self._children()[self.B]),
+                        dtype=torch.float32)
+        return cast_to_storage(x.reshape(self.B * self.chunk, self.H_q, self.D), self.kv_dtype)
+
+    def flops(self) -> int:
+        """Algorithmic flops of one launch: 2 D for q.k and 2 D for p.v per (query
+        row, visible position); causal: row i of a chunk sees cached + i + 1."""
+        if self.causal:
+            visible = self.chunk * self.cached + self.chunk * (self.chunk + 1) // 2
+        else:
+            visible = self.chunk * self.n
+        return self.B * self.H_q * visible * 4 * self.D
+
+    def kv_bytes(self) -> int:
+        """K+V bytes of the contexts (each read at least once)."""
+        return self.B * self.n * self.H_kv * self.D * 2 * ELEM_BYTES[self.kv_dtype]
+
+
+def make_prefill(name: str) -> PrefillWorkload:
+    """prefill8b: Llama-3-8B heads (32 q / 8 kv, d 128), bf16, 16 sequences of
+    2048 cached tokens plus a 512-token chunk, causal."""
+    if name == "prefill8b":
+        return PrefillWorkload(name, 6, 16, 32, 8, 128, BF16, 2048, 512)
+    raise ValueError(f"unknown prefill workload {name!r}")
