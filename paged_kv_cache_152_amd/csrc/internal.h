@@ -77,6 +77,7 @@ struct PrefillParams {
     const int32_t* lens;      // [n_seqs] context lengths including the chunk
     int32_t n_seqs, total_q, H_q, H_kv, G, D, num_blocks, max_blocks;
     int32_t gs;               // query heads per row group (divides G, at most 16)
+    int64_t tiles;            // query tiles per (sequence, head group), set by the launcher
     int32_t kv_dt, q_dt, causal;
     float scale;
 };
@@ -97,6 +98,7 @@ hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 bool prefill_supported(int32_t kv_dt, int32_t q_dt, int32_t D);
 int prefill_heads_per_group(int32_t G);
 int64_t prefill_tiles(int32_t G, int32_t max_q_len);
+int64_t prefill_workgroups(int32_t G, int32_t H_kv, int32_t n_seqs, int32_t max_q_len);
 hipError_t launch_prefill(const PrefillParams& p, int32_t max_q_len, hipStream_t stream);
 
 }  // namespace pkv

@@ -908,7 +908,8 @@ int paged_prefill(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t n_seqs, 
     const int32_t G = H_q / p->kv_heads;
     const int32_t gs = pkv::prefill_heads_per_group(G);
     if ((int64_t)p->kv_heads * (G / gs) > 65535) return fail(PKV_ERR_INVALID_ARG, "too many query heads for one launch");
-    if (pkv::prefill_tiles(G, max_q_len) > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "max_q_len too large");
+    if (pkv::prefill_workgroups(G, p->kv_heads, n_seqs, max_q_len) > INT32_MAX)
+        return fail(PKV_ERR_INVALID_ARG, "max_q_len too large");
     const bool work = n_seqs > 0 && total_q > 0 && max_q_len > 0;
     if (work && (!q || !out || !q_start || !block_tables || !context_lens))
         return fail(PKV_ERR_INVALID_ARG, "NULL device pointer");

@@ -6,26 +6,31 @@
 // cores.
 //
 // Work split.  A workgroup of 4 waves takes one (query tile, head group,
-// sequence).  A wave owns 16 query rows: TW = 16 / gs query tokens times the gs
-// query heads of one KV head group (row c = token c / gs, head c % gs; rows
-// beyond TW * gs are padding).  The four waves walk the same 16-token blocks
-// of the context; their K and V tiles come from HBM once per workgroup.
+// sequence); the workgroups of one (sequence, head group) are placed on one XCD
+// so its L2 serves their repeated reads of the same K/V.  A wave owns 32 query
+// rows in two groups of 16: tw = 32 / gs query tokens times the gs query heads
+// of one KV head group (row = token * gs + head; rows beyond tw * gs are
+// padding).  The four waves walk the same 16-token blocks of the context.
+// Each thread moves 1/256 of a block's K and V tile from HBM into registers
+// four blocks ahead of use, then into LDS: K as it is stored ([token][dim],
+// rows padded against bank conflicts), V transposed ([dim][token]).  Block ids
+// come from a per-wave register of 64 table entries.
 //
-// Per block, with m = 16 tokens:
+// Per block, with m = 16 tokens, for each row group:
 //   S^T = K . Q^T    4 (head_dim 128) or 2 (64) v_mfma_f32_16x16x32: A = the K
-//                    tile (lane: token l % 16, 8 dims), straight from HBM;
-//                    B = the 16 query rows (lane: row l % 16, 8 dims), held
-//                    in registers for the whole walk.  Lane l ends with the
-//                    logits of tokens 4 (l / 16) .. +3 for row l % 16.
+//                    tile (lane: token l % 16, 8 dims) from LDS, shared by the
+//                    row groups; B = 16 query rows (lane: row l % 16, 8 dims),
+//                    held in registers for the whole walk.  Lane l ends with
+//                    the logits of tokens 4 (l / 16) .. +3 for row l % 16.
 //   online softmax   the running max / sum of a row live in the four lanes
 //                    l % 16 = row; two cross-row shuffles per block.  Logits
 //                    are in base 2 (exp2), q's scale folded in.
 //   O^T += V^T . P^T head_dim / 16 v_mfma_f32_16x16x16: B = P^T, which is
 //                    exactly the layout S^T left in the lanes (packed to
-//                    16-bit), A = V^T read from LDS, where the workgroup
-//                    wrote the block's V transposed ([dim][token]) once.
-// Lane l accumulates output dims 16 mt + 4 (l / 16) + i of row l % 16, so the
-// rescale when a row's max moves is one multiply per accumulator.
+//                    16-bit), A = V^T from LDS, shared by the row groups.
+// Lane l accumulates output dims 16 mt + 4 (l / 16) + i of row l % 16 of each
+// group, so the rescale when a row's max moves is one multiply per
+// accumulator.
 //
 // FP8 pools: K codes are widened exactly to q's 16-bit type for Q.K^T; V codes
 // to f16 (exact) for P.V, with P in f16.  The K scale folds into the logit
@@ -123,53 +128,75 @@ __device__ __forceinline__ float across_rows_sum(float v) {
     return v + __shfl_xor(v, 32, 64);
 }
 
+// Rows per wave: kRowGroups groups of 16; tiles of K / V staged NR blocks ahead.
+constexpr int kRowGroups = 2;
+constexpr int kAhead = 4;
+
+// Workgroups of one (sequence, head group) walk the same K/V; keep them on one
+// XCD (workgroups are dealt round-robin over the 8 XCDs), so its L2 serves the
+// repeats.  Logical index = xcd * (n / 8) + position on that XCD.
+__device__ __forceinline__ int64_t xcd_logical(int64_t i, int64_t n) {
+    const int64_t full = n - n % 8;
+    if (i >= full) return i;
+    return (i % 8) * (full / 8) + i / 8;
+}
+
 template <int KDT, int QDT, int D>
 __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillParams p) {
     constexpr int KS = D / 32;                 // S^T steps (32 dims each)
     constexpr int MT = D / 16;                 // O^T m-tiles (16 dims each)
-    constexpr int EPL = D / 16;                // V dims one lane stages per block
+    constexpr int R = kRowGroups;
     constexpr int PT = KDT == DT_BF16 ? DT_BF16 : DT_F16;   // type of P and V in P.V
+    constexpr int KT = KDT == DT_FP8 ? QDT : KDT;            // type of K in Q.K^T
     constexpr int KE = KDT == DT_FP8 ? 1 : 2;  // bytes per stored K/V element
+    constexpr int EPL = D / 16;                // elements of a tile one thread stages (16 threads a token)
+    constexpr int KROW = D + 8;                // LDS K row, padded (16-bit elements)
+    constexpr int VROW = 20;                   // LDS V^T row: 16 tokens + padding
     using QV = typename Vec8<QDT>::T;
-    // V^T of the current and the next block, [dim][token], 16-bit values of PT
-    __shared__ uint16_t vt[2][D][16];
+    __shared__ __align__(16) uint16_t ks_lds[2][16 * KROW];
+    __shared__ __align__(16) uint16_t vt_lds[2][D * VROW];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane >> 4, c = lane & 15;
-    const int s = blockIdx.z;
-    const int gs = p.gs, subs = p.G / gs, TW = 16 / gs;
-    const int g = blockIdx.y / subs;
-    const int hq0 = g * p.G + (blockIdx.y % subs) * gs;
+    const int gs = p.gs, subs = p.G / gs;
+    const int tw = (16 * R) / gs;                            // query tokens per wave
+    const int64_t tiles = p.tiles;
+    const int64_t n_wg = tiles * p.H_kv * subs * p.n_seqs;
+    const int64_t L = xcd_logical(blockIdx.x, n_wg);
+    const int tile = (int)(L % tiles);
+    const int hgi = (int)((L / tiles) % ((int64_t)p.H_kv * subs));
+    const int s = (int)(L / (tiles * p.H_kv * subs));
+    const int g = hgi / subs;
+    const int hq0 = g * p.G + (hgi % subs) * gs;
 
     const int q0 = min(p.q_start[s], p.total_q), q1 = min(max(p.q_start[s + 1], q0), p.total_q);
     const int q_len = q1 - q0;
     int n = p.lens[s];
     n = n < 0 ? 0 : (n > p.max_blocks * kBlock ? p.max_blocks * kBlock : n);
-    const int tile0 = blockIdx.x * kPfWaves * TW;            // first query token of the workgroup
+    const int tile0 = tile * kPfWaves * tw;                 // first query token of the workgroup
     if (tile0 >= q_len) return;
-    const int tile_last = min(q_len, tile0 + kPfWaves * TW) - 1;
-
-    // this lane's query row
-    const int i_row = tile0 + wave * TW + c / gs;            // token index within the chunk
-    const int h_row = hq0 + c % gs;
-    const bool row_live = c < TW * gs && i_row < q_len;
-    const int pos = n - q_len + i_row;                       // the row's position in the context
-    const int see = p.causal ? pos : n - 1;                  // newest position the row sees
-
-    // the blocks the workgroup needs
+    const int tile_last = min(q_len, tile0 + kPfWaves * tw) - 1;
     const int wg_see = p.causal ? n - q_len + tile_last : n - 1;
     const int nblk = wg_see < 0 ? 0 : min((wg_see + kBlock) / kBlock, (n + kBlock - 1) / kBlock);
 
-    // Q^T operand: row c, dims 32 k + 8 r .. +7
-    QV qb[KS];
-    {
-        const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q);
-        const int64_t qrow = ((int64_t)(q0 + i_row) * p.H_q + h_row) * D;
+    // this lane's query rows: group rg holds row rg * 16 + c of the wave
+    int i_row[R], see[R];
+    bool live[R];
+    QV qb[R][KS];
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q);
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) {
+        const int row = rg * 16 + c;
+        i_row[rg] = tile0 + wave * tw + row / gs;
+        live[rg] = row < tw * gs && i_row[rg] < q_len;
+        const int pos = n - q_len + i_row[rg];
+        see[rg] = p.causal ? pos : n - 1;
+        const int64_t qrow = ((int64_t)(q0 + i_row[rg]) * p.H_q + hq0 + row % gs) * D;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-            if (row_live) raw = *reinterpret_cast<const uint4*>(q16 + qrow + 32 * k + 8 * r);
-            qb[k] = __builtin_bit_cast(QV, raw);
+            if (live[rg]) raw = *reinterpret_cast<const uint4*>(q16 + qrow + 32 * k + 8 * r);
+            qb[rg][k] = __builtin_bit_cast(QV, raw);
         }
     }
     float qscale = p.scale * kLog2e;
@@ -182,126 +209,170 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillPar
     const int32_t* table = p.tables + (int64_t)s * p.max_blocks;
     const char* kbase = reinterpret_cast<const char*>(p.k_pool);
     const char* vbase = reinterpret_cast<const char*>(p.v_pool);
-    constexpr int ROW = D * KE;                              // bytes of a token row
-    constexpr int TILE = kBlock * ROW;                       // bytes of a (block, head) tile
+    constexpr int ROW = D * KE;
+    constexpr int TILE = kBlock * ROW;
     const int64_t blk_stride = (int64_t)p.H_kv * TILE;
     const int64_t head_off = (int64_t)g * TILE;
-    // K operand of this lane: token c, dims 32 k + 8 r; V staging: token tid / 16, dims EPL (tid % 16)
-    const int k_off = c * ROW + 8 * r * KE;
-    const int v_tok = tid >> 4, v_dim = (tid & 15) * EPL;
-    const int v_off = v_tok * ROW + v_dim * KE;
-
-    using KRaw = std::conditional_t<KDT == DT_FP8, uint2, uint4>;                 // 8 K elements
-    using VRaw = std::conditional_t<EPL * KE == 16, uint4, std::conditional_t<EPL * KE == 8, uint2, uint32_t>>;
+    // staging: thread tid moves token tid / 16, elements EPL (tid % 16) .. +EPL-1 of the K and V tiles
+    const int st_tok = tid >> 4, st_el = (tid & 15) * EPL;
+    const int st_off = st_tok * ROW + st_el * KE;
+    using Raw = std::conditional_t<EPL * KE == 16, uint4, std::conditional_t<EPL * KE == 8, uint2, uint32_t>>;
     struct Stage {
-        KRaw k[KS];
-        VRaw v;
+        Raw k, v;
         bool ok;
     };
+    int tv = -1;                               // table entries of blocks 64 t .. 64 t + 63, one per lane
+    int tv_base = -64;
     auto fetch = [&](int j, Stage& st) {
-        const int phys = table[j];
+        if (j - tv_base >= 64) {               // uniform: every lane walks the same j
+            tv_base = j & ~63;
+            tv = tv_base + lane < nblk ? table[tv_base + lane] : -1;
+        }
+        const int phys = __builtin_amdgcn_readlane(tv, j & 63);
         st.ok = phys >= 0 && phys < p.num_blocks;
         if (!st.ok) return;
-        const int64_t off = (int64_t)phys * blk_stride + head_off;
-#pragma unroll
-        for (int k = 0; k < KS; ++k) st.k[k] = *reinterpret_cast<const KRaw*>(kbase + off + k_off + 32 * k * KE);
-        st.v = *reinterpret_cast<const VRaw*>(vbase + off + v_off);
+        const int64_t off = (int64_t)phys * blk_stride + head_off + st_off;
+        st.k = *reinterpret_cast<const Raw*>(kbase + off);
+        st.v = *reinterpret_cast<const Raw*>(vbase + off);
     };
-    // V rows of the block, transposed into LDS as PT values; dead rows are zero
-    auto stage_v = [&](int j, const Stage& st, int buf) {
-        uint16_t e16[EPL];
-        const bool live = st.ok && j * kBlock + v_tok < n;
+    // K tile natural ([token][dim], K's MFMA type), V tile transposed ([dim][token], PT); dead rows zero
+    auto stage = [&](int j, const Stage& st, int buf) {
+        const bool ok = st.ok && j * kBlock + st_tok < n;
+        uint16_t ke[EPL], ve[EPL];
         if constexpr (KDT == DT_FP8) {
-            // EPL codes -> f16
-            uint32_t w[EPL / 2];
             if constexpr (EPL == 8) {
-                const uint4 f = fp8x8_to<DT_F16>(*reinterpret_cast<const uint2*>(&st.v));
-                w[0] = f.x; w[1] = f.y; w[2] = f.z; w[3] = f.w;
-            } else {
-                const uint32_t code = *reinterpret_cast<const uint32_t*>(&st.v);
-                w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false));
-                w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, true));
-            }
+                const uint4 kw = fp8x8_to<KT>(*reinterpret_cast<const uint2*>(&st.k));
+                const uint4 vw = fp8x8_to<DT_F16>(*reinterpret_cast<const uint2*>(&st.v));
+                const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
-            for (int e = 0; e < EPL / 2; ++e) {
-                e16[2 * e] = (uint16_t)(w[e] & 0xFFFFu);
-                e16[2 * e + 1] = (uint16_t)(w[e] >> 16);
+                for (int e = 0; e < 4; ++e) {
+                    ke[2 * e] = (uint16_t)kk[e]; ke[2 * e + 1] = (uint16_t)(kk[e] >> 16);
+                    ve[2 * e] = (uint16_t)vv[e]; ve[2 * e + 1] = (uint16_t)(vv[e] >> 16);
+                }
+            } else {
+                const uint32_t kc = *reinterpret_cast<const uint32_t*>(&st.k);
+                const uint32_t vc = *reinterpret_cast<const uint32_t*>(&st.v);
+                uint32_t kk[2], vv[2];
+                if constexpr (KT == DT_BF16) {
+                    kk[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kc, 1.0f, false));
+                    kk[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kc, 1.0f, true));
+                } else {
+                    kk[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kc, 1.0f, false));
+                    kk[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kc, 1.0f, true));
+                }
+                vv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vc, 1.0f, false));
+                vv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vc, 1.0f, true));
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    ke[2 * e] = (uint16_t)kk[e]; ke[2 * e + 1] = (uint16_t)(kk[e] >> 16);
+                    ve[2 * e] = (uint16_t)vv[e]; ve[2 * e + 1] = (uint16_t)(vv[e] >> 16);
+                }
             }
         } else {
-            const uint32_t* w = reinterpret_cast<const uint32_t*>(&st.v);
+            const uint32_t* kw = reinterpret_cast<const uint32_t*>(&st.k);
+            const uint32_t* vw = reinterpret_cast<const uint32_t*>(&st.v);
 #pragma unroll
             for (int e = 0; e < EPL / 2; ++e) {
-                e16[2 * e] = (uint16_t)(w[e] & 0xFFFFu);
-                e16[2 * e + 1] = (uint16_t)(w[e] >> 16);
+                ke[2 * e] = (uint16_t)kw[e]; ke[2 * e + 1] = (uint16_t)(kw[e] >> 16);
+                ve[2 * e] = (uint16_t)vw[e]; ve[2 * e + 1] = (uint16_t)(vw[e] >> 16);
             }
         }
+        uint32_t kp[EPL / 2];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) vt[buf][v_dim + e][v_tok] = live ? e16[e] : (uint16_t)0;
+        for (int e = 0; e < EPL / 2; ++e)
+            kp[e] = ok ? (uint32_t)ke[2 * e] | ((uint32_t)ke[2 * e + 1] << 16) : 0u;
+        uint16_t* kd = &ks_lds[buf][st_tok * KROW + st_el];
+        if constexpr (EPL == 8) *reinterpret_cast<uint4*>(kd) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
+        else *reinterpret_cast<uint2*>(kd) = make_uint2(kp[0], kp[1]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vt_lds[buf][(st_el + e) * VROW + st_tok] = ok ? ve[e] : (uint16_t)0;
     };
 
-    f32x4_t acc[MT];
+    f32x4_t acc[R][MT];
+    float m_run[R], l_run[R];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    Stage cur, nxt;
-    if (nblk > 0) fetch(0, cur);
-    for (int j = 0; j < nblk; ++j) {
-        const int buf = j & 1;
-        stage_v(j, cur, buf);
-        if (j + 1 < nblk) fetch(j + 1, nxt);                 // in flight during this block's math
-        __syncthreads();                                     // V^T of block j is in LDS
-
-        // S^T = K . Q^T
-        f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int rg = 0; rg < R; ++rg) {
+        m_run[rg] = -INFINITY;
+        l_run[rg] = 0.0f;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            QV a;
-            if constexpr (KDT == DT_FP8) a = __builtin_bit_cast(QV, fp8x8_to<QDT>(cur.k[k]));
-            else a = __builtin_bit_cast(QV, cur.k[k]);
-            S = mma_k32<QDT>(a, qb[k], S);
-        }
-        const int tok = j * kBlock + 4 * r;                  // token of S[0] in this lane
-        float z[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool vis = cur.ok && row_live && tok + i < n && tok + i <= see;
-            z[i] = vis ? S[i] * qscale : -INFINITY;          // select, never 0 * garbage
-        }
-        const float m_blk = across_rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-        const float m_new = fmaxf(m_run, m_blk);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float pr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_use);
-        l_run = fmaf(l_run, alpha, across_rows_sum((pr[0] + pr[1]) + (pr[2] + pr[3])));
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-        }
-        // O^T += V^T . P^T
-        const uint2 pb = make_uint2(pack2<PT>(pr[0], pr[1]), pack2<PT>(pr[2], pr[3]));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const uint2 va = *reinterpret_cast<const uint2*>(&vt[buf][16 * mt + c][4 * r]);
-            acc[mt] = mma_k16<PT>(va, pb, acc[mt]);
-        }
-        cur = nxt;
+        for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    if (!row_live) return;
-    const float inv = l_run > 0.0f ? vscale / l_run : 0.0f;
+    auto compute = [&](int j, int buf) {
+        // K operand (token c, dims 32 k + 8 r), shared by the row groups
+        typename Vec8<KT>::T ka[KS];
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+            ka[k] = *reinterpret_cast<const typename Vec8<KT>::T*>(&ks_lds[buf][c * KROW + 32 * k + 8 * r]);
+        const int tok = j * kBlock + 4 * r;
+        uint2 pb[R];
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) {
+            f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < KS; ++k) S = mma_k32<QDT>(__builtin_bit_cast(QV, ka[k]), qb[rg][k], S);
+            float z[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool vis = live[rg] && tok + i < n && tok + i <= see[rg];
+                z[i] = vis ? S[i] * qscale : -INFINITY;      // select, never 0 * garbage
+            }
+            const float m_blk = across_rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+            const float m_new = fmaxf(m_run[rg], m_blk);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run[rg] - m_use);
+            float pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_use);
+            l_run[rg] = fmaf(l_run[rg], alpha, across_rows_sum((pr[0] + pr[1]) + (pr[2] + pr[3])));
+            m_run[rg] = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[rg][mt] *= alpha;
+            }
+            pb[rg] = make_uint2(pack2<PT>(pr[0], pr[1]), pack2<PT>(pr[2], pr[3]));
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint2 va = *reinterpret_cast<const uint2*>(&vt_lds[buf][(16 * mt + c) * VROW + 4 * r]);
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg) acc[rg][mt] = mma_k16<PT>(va, pb[rg], acc[rg][mt]);
+        }
+    };
+
+    // register ring of kAhead blocks in flight; LDS double buffer for the block in use
+    Stage ring[kAhead];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k)
+        if (k < nblk) fetch(k, ring[k]);
+    for (int j0 = 0; j0 < nblk; j0 += kAhead) {
+#pragma unroll
+        for (int k = 0; k < kAhead; ++k) {
+            const int j = j0 + k;
+            if (j < nblk) {
+                stage(j, ring[k], j & 1);
+                if (j + kAhead < nblk) fetch(j + kAhead, ring[k]);
+                __syncthreads();                             // tiles of block j are in LDS
+                compute(j, j & 1);
+            }
+        }
+    }
+
     uint16_t* o16 = reinterpret_cast<uint16_t*>(p.out);
-    const int64_t orow = ((int64_t)(q0 + i_row) * p.H_q + h_row) * D;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        uint16_t e[4];
+    for (int rg = 0; rg < R; ++rg) {
+        if (!live[rg]) continue;
+        const int row = rg * 16 + c;
+        const float inv = l_run[rg] > 0.0f ? vscale / l_run[rg] : 0.0f;
+        const int64_t orow = ((int64_t)(q0 + i_row[rg]) * p.H_q + hq0 + row % gs) * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = to_q16<QDT>(acc[mt][i] * inv);
-        *reinterpret_cast<uint2*>(o16 + orow + 16 * mt + 4 * r) =
-            make_uint2((uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16));
+        for (int mt = 0; mt < MT; ++mt) {
+            uint16_t e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] = to_q16<QDT>(acc[rg][mt][i] * inv);
+            *reinterpret_cast<uint2*>(o16 + orow + 16 * mt + 4 * r) =
+                make_uint2((uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16));
+        }
     }
 }
 
@@ -336,21 +407,25 @@ int prefill_heads_per_group(int32_t G) {
 }
 
 int64_t prefill_tiles(int32_t G, int32_t max_q_len) {
-    const int tw = 16 / prefill_heads_per_group(G);
+    const int tw = (16 * kRowGroups) / prefill_heads_per_group(G);
     const int per_wg = kPfWaves * tw;
     return ((int64_t)max_q_len + per_wg - 1) / per_wg;
+}
+
+int64_t prefill_workgroups(int32_t G, int32_t H_kv, int32_t n_seqs, int32_t max_q_len) {
+    return prefill_tiles(G, max_q_len) * H_kv * (G / prefill_heads_per_group(G)) * n_seqs;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int32_t max_q_len, hipStream_t stream) {
     KernelFn fn = pick(p.kv_dt, p.q_dt, p.D);
     if (!fn) return hipErrorInvalidValue;
-    const int64_t tiles = prefill_tiles(p.G, max_q_len);
-    if (tiles <= 0 || p.n_seqs <= 0) return hipSuccess;
+    const int64_t n_wg = prefill_workgroups(p.G, p.H_kv, p.n_seqs, max_q_len);
+    if (n_wg <= 0) return hipSuccess;
     PrefillParams arg = p;
+    arg.tiles = prefill_tiles(p.G, max_q_len);
     void* args[] = {&arg};
-    const unsigned groups = (unsigned)((int64_t)p.H_kv * (p.G / p.gs));
-    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)tiles, groups, (unsigned)p.n_seqs),
-                           dim3(kPfWaves * 64), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n_wg), dim3(kPfWaves * 64), args, 0,
+                           stream);
 }
 
 }  // namespace pkv
