@@ -319,6 +319,38 @@ int paged_decode_set_partition(kv_pool_t* pool, int32_t partition_tokens);
 int32_t paged_decode_partition_tokens(const kv_pool_t* pool, int32_t B, int32_t H_q,
                                       int32_t max_context_len);
 
+/* ---------------------------------------------------------------------------
+ * Swap ([cf1] §2.2: demand paging; blocks not in use may live in host memory
+ * and come back when needed).  A whole sequence at a time.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes a swapped copy of the sequence takes: ceil(len / block_size) blocks x
+ * 2 x kv_heads x block_bytes.  Layout of the copy: for each logical block in
+ * order, its K tiles of all KV heads, then its V tiles
+ * ([kv_heads][block_size][head_dim] each, the pool's storage type).
+ * Errors: INVALID_ARG, STATE. */
+int kv_seq_swap_bytes(const kv_pool_t* pool, int32_t seq, size_t* bytes);
+
+/* Copy the sequence's blocks to host_dst (host memory of at least
+ * kv_seq_swap_bytes; pinned memory copies fastest) and release them as
+ * kv_seq_free would (shared blocks stay with their other holders, cached
+ * prefix blocks become evictable).  Owed copy-on-write copies run first.
+ * The sequence keeps its id and length but cannot grow, fork, be registered
+ * or appear in kv_block_tables until swapped in; kv_seq_free works either
+ * way.  Synchronous: returns when host_dst holds the data (work queued
+ * earlier on `stream` is waited for).  A metadata-only pool moves no data
+ * (the buffer is ignored and may be NULL).  Errors: INVALID_ARG (buffer too small, NULL),
+ * STATE (unknown or already swapped), DEVICE. */
+int kv_seq_swap_out(kv_pool_t* pool, int32_t seq, void* host_dst, size_t bytes, void* stream);
+
+/* Bring a swapped sequence back: ceil(len / block_size) fresh blocks, all or
+ * nothing, in logical order (each the sequence's own; sharing and prefix-
+ * cache keys it had are not restored), filled from host_src (the layout
+ * kv_seq_swap_out wrote).  Synchronous.  Errors: INVALID_ARG, NO_BLOCKS
+ * (nothing changed), STATE (not swapped out), DEVICE (the blocks are given
+ * back and the sequence stays out). */
+int kv_seq_swap_in(kv_pool_t* pool, int32_t seq, const void* host_src, size_t bytes, void* stream);
+
 /* Multi-query attention through block tables: a chunk of prompt tokens per
  * sequence attending to the cached context and to itself (the prefill stage of
  * [mlqm] 三, and chunked prefill of [mlqm] 七, over the paged cache of [cf1]

@@ -27,6 +27,12 @@ What the pages leave open, and the reading taken here:
     old block loses one holder.  The copy block is taken before any new block.
   * Reserve is all-or-nothing: without enough free blocks nothing changes.
   * Slot of logical position p: table[p // bs] * bs + p % bs.
+  * Swap ([cf1] §2.2 demand paging: blocks not in use may live in host memory
+    and are brought back when needed): swap-out releases a sequence's blocks
+    exactly as freeing it would (deepest first) but keeps the sequence, its
+    length and its token contents (on the host); swap-in takes ceil(n / bs)
+    fresh blocks, all or nothing, in logical order.  A swapped sequence
+    cannot grow, fork, be registered or appear in a table until swapped in.
   * Prefix cache ([cf1] §3.3 content hash per block; [lqnn] §3 the cache
     identity includes the model/tenant namespace): full block i of a prompt
     has key_i = H(key_{i-1}, ns, its 16 tokens), key_{-1} = 0, with H the
@@ -83,6 +89,7 @@ class BlockPoolModel:
         self.cache = {}         # content key -> block
         self.key_of = {}        # cached block -> (key, tokens)
         self.lru = []           # cached blocks nobody holds, oldest release first
+        self.swapped = set()    # sequences whose blocks live on the host
 
     def _take(self) -> int:
         if self.free:
@@ -111,10 +118,37 @@ class BlockPoolModel:
         self.seqs[sid] = [[], 0]
         return sid
 
-    def _get(self, sid):
+    def _get(self, sid, resident: bool = True):
         if sid not in self.seqs:
             raise AllocError(STATE, f"unknown or freed sequence {sid}")
+        if resident and sid in self.swapped:
+            raise AllocError(STATE, f"sequence {sid} is swapped out")
         return self.seqs[sid]
+
+    # -- swap ----------------------------------------------------------------
+    def swap_out(self, sid: int) -> int:
+        """Release the blocks of sid (deepest first); returns how many it held."""
+        blocks, _ = self._get(sid)
+        n = len(blocks)
+        for b in reversed(blocks):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self._release(b)
+        self.seqs[sid][0] = []
+        self.swapped.add(sid)
+        return n
+
+    def swap_in(self, sid: int):
+        """Fresh blocks for every block of sid, all or nothing; returns the table."""
+        if sid not in self.seqs or sid not in self.swapped:
+            raise AllocError(STATE, f"sequence {sid} is not swapped out")
+        length = self.seqs[sid][1]
+        need = -(-length // self.bs)
+        if need > self.available():
+            raise AllocError(NO_BLOCKS, "not enough free blocks")
+        self.seqs[sid][0] = [self._take() for _ in range(need)]
+        self.swapped.discard(sid)
+        return list(self.seqs[sid][0])
 
     def reserve(self, sid: int, n: int):
         """Append n token positions; return their slots."""
@@ -152,7 +186,8 @@ class BlockPoolModel:
         return sid
 
     def free_seq(self, sid: int) -> None:
-        blocks, _ = self._get(sid)
+        blocks, _ = self._get(sid, resident=False)
+        self.swapped.discard(sid)
         for b in reversed(blocks):
             self.ref[b] -= 1
             assert self.ref[b] >= 0
@@ -203,7 +238,7 @@ class BlockPoolModel:
 
     # -- queries -----------------------------------------------------------
     def length(self, sid: int) -> int:
-        return self._get(sid)[1]
+        return self._get(sid, resident=False)[1]
 
     def table(self, sid: int):
         return list(self._get(sid)[0])
@@ -237,7 +272,10 @@ class BlockPoolModel:
     # -- invariants ([cf1] §3.2, §3.3) ----------------------------------------
     def check_invariants(self) -> None:
         holders = [0] * self.N
-        for blocks, length in self.seqs.values():
+        for sid, (blocks, length) in self.seqs.items():
+            if sid in self.swapped:
+                assert blocks == [], "a swapped sequence holds blocks"
+                continue
             assert len(blocks) == -(-length // self.bs), "blocks != ceil(len / bs)"
             for b in blocks:
                 holders[b] += 1

@@ -89,6 +89,9 @@ _SIGNATURES = {
     "paged_decode": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, ctypes.c_float,
                                     _P, _P, ctypes.c_size_t, _P]),
     "paged_decode_workspace_bytes": (ctypes.c_size_t, [_P, _I32, _I32, _I32]),
+    "kv_seq_swap_bytes": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "kv_seq_swap_out": (ctypes.c_int, [_P, _I32, _P, ctypes.c_size_t, _P]),
+    "kv_seq_swap_in": (ctypes.c_int, [_P, _I32, _P, ctypes.c_size_t, _P]),
     "paged_prefill": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I32, _I32, _P, _I32, _P, ctypes.c_float,
                                      _I32, _P, _P]),
     "paged_decode_set_partition": (ctypes.c_int, [_P, _I32]),
@@ -375,6 +378,32 @@ class KVPool:
                                   int(max_context_len), float(scale), op, wp, wbytes, _stream(stream)),
                "paged_decode")
         return out
+
+    def swap_bytes(self, seq: int) -> int:
+        n = ctypes.c_size_t()
+        _check(lib().kv_seq_swap_bytes(self.handle, seq, ctypes.byref(n)), "kv_seq_swap_bytes")
+        return n.value
+
+    def swap_out(self, seq: int, host=None, stream=None):
+        """kv_seq_swap_out into `host` (a CPU tensor, pinned is fastest; allocated
+        pinned if None; none on a metadata-only pool).  Returns the host tensor."""
+        torch = _torch()
+        nbytes = self.swap_bytes(seq)
+        if host is None and not self.host_only:
+            host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        ptr, size = (None, 0) if host is None else (ctypes.c_void_p(host.data_ptr()), host.numel() * host.element_size())
+        if host is not None and (host.is_cuda or not host.is_contiguous()):
+            raise ValueError("host must be a contiguous CPU tensor")
+        _check(lib().kv_seq_swap_out(self.handle, seq, ptr, size, None if self.host_only else _stream(stream)),
+               "kv_seq_swap_out")
+        return host
+
+    def swap_in(self, seq: int, host=None, stream=None) -> None:
+        ptr, size = (None, 0) if host is None else (ctypes.c_void_p(host.data_ptr()), host.numel() * host.element_size())
+        if host is not None and (host.is_cuda or not host.is_contiguous()):
+            raise ValueError("host must be a contiguous CPU tensor")
+        _check(lib().kv_seq_swap_in(self.handle, seq, ptr, size, None if self.host_only else _stream(stream)),
+               "kv_seq_swap_in")
 
     def prefill(self, q, q_start, block_tables, context_lens, max_q_len: int, scale: float, causal: bool = True,
                 out=None, stream=None):

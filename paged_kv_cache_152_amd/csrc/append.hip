@@ -136,7 +136,32 @@ __global__ __launch_bounds__(256) void kv_copy_blocks(CopyParams p) {
     dst[j] = src[j];
 }
 
+// Swap staging: blockIdx.y selects the block, 16 bytes per thread over its
+// K tile then its V tile.
+__global__ __launch_bounds__(256) void kv_move_blocks(MoveParams p) {
+    const int b = blockIdx.y;
+    const int64_t n16 = p.block_bytes / 16;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= p.n || i >= 2 * n16) return;
+    const bool v = i >= n16;
+    const int64_t j = v ? i - n16 : i;
+    uint4* pool = reinterpret_cast<uint4*>(reinterpret_cast<char*>(v ? p.v_pool : p.k_pool) +
+                                           (int64_t)p.ids[b] * p.block_bytes) + j;
+    uint4* stage = reinterpret_cast<uint4*>(p.staging + (p.first + b) * 2 * p.block_bytes + (v ? p.block_bytes : 0)) + j;
+    if (p.to_pool) *pool = *stage;
+    else *stage = *pool;
+}
+
 }  // namespace
+
+hipError_t launch_move_blocks(const MoveParams& p, hipStream_t stream) {
+    if (p.n <= 0) return hipSuccess;
+    MoveParams arg = p;
+    void* args[] = {&arg};
+    const int64_t threads = 2 * (p.block_bytes / 16);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kv_move_blocks),
+                           dim3((unsigned)((threads + 255) / 256), (unsigned)p.n), dim3(256), args, 0, stream);
+}
 
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream) {
     if (p.n <= 0) return hipSuccess;

@@ -65,6 +65,19 @@ struct DecodeParams {
     float scale;              // softmax scale as given
 };
 
+// Swap: whole blocks (all KV heads, K and V) between the pools and a staging
+// buffer laid out [block][K tile bytes | V tile bytes], in logical order.
+struct MoveParams {
+    int32_t ids[kMaxCopiesPerLaunch];   // physical blocks of this launch
+    int32_t n;
+    int64_t first;                      // staging slot of ids[0]
+    void* k_pool;
+    void* v_pool;
+    char* staging;
+    int64_t block_bytes;
+    int32_t to_pool;                    // 0: pools -> staging, 1: staging -> pools
+};
+
 struct PrefillParams {
     const void* k_pool;
     const void* v_pool;
@@ -95,6 +108,7 @@ hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
+hipError_t launch_move_blocks(const MoveParams& p, hipStream_t stream);
 bool prefill_supported(int32_t kv_dt, int32_t q_dt, int32_t D);
 int prefill_heads_per_group(int32_t G);
 int64_t prefill_tiles(int32_t G, int32_t max_q_len);

@@ -55,6 +55,7 @@ int hip_fail(hipError_t e, const char* what) {
 struct Seq {
     std::vector<int32_t> blocks;
     int32_t len = 0;
+    bool swapped = false;      // blocks live on the host (kv_seq_swap_out); `blocks` is empty
 };
 
 constexpr int kMaxTimed = 65536;
@@ -94,6 +95,10 @@ struct kv_pool {
     std::vector<std::array<int32_t, 16>> block_tokens;
     std::list<int32_t> lru;
     std::vector<std::list<int32_t>::iterator> lru_pos;
+
+    // device staging of swaps, grown on demand
+    void* staging = nullptr;
+    size_t staging_bytes = 0;
 
     bool profiling = false;
     std::vector<KernelTimer> timers;
@@ -304,6 +309,7 @@ int kv_pool_destroy(kv_pool_t* pool) {
         if (pool->k_pool) hipFree(pool->k_pool);
         if (pool->v_pool) hipFree(pool->v_pool);
         if (pool->scales) hipFree(pool->scales);
+        if (pool->staging) hipFree(pool->staging);
     }
     delete pool;
     return ok();
@@ -374,6 +380,7 @@ int kv_seq_reserve(kv_pool_t* p, int32_t seq, int32_t n_tokens, int32_t* slots) 
     if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
     Seq* s = find_seq(p, seq);
     if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
+    if (s->swapped) return fail(PKV_ERR_STATE, "sequence %d is swapped out", seq);
     if (n_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "n_tokens < 0");
     if (n_tokens > 0 && !slots) return fail(PKV_ERR_INVALID_ARG, "slot_mapping_out is NULL");
     const int64_t new_len = (int64_t)s->len + n_tokens;
@@ -426,6 +433,7 @@ int kv_batch_reserve(kv_pool_t* p, const int32_t* seqs, int32_t n, const int32_t
             if (k < 0) return fail(PKV_ERR_INVALID_ARG, "n_tokens[%d] < 0", i);
             const Seq* s = find_seq(p, seqs[i]);
             if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seqs[i]);
+            if (s->swapped) return fail(PKV_ERR_STATE, "sequence %d is swapped out", seqs[i]);
             auto it = len.find(seqs[i]);
             const int64_t cur = it == len.end() ? s->len : it->second;
             const int64_t nxt = cur + k;
@@ -463,6 +471,7 @@ int kv_seq_fork(kv_pool_t* p, int32_t parent, int32_t n_shared, int32_t* child) 
     if (!p || !child) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
     Seq* s = find_seq(p, parent);
     if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", parent);
+    if (s->swapped) return fail(PKV_ERR_STATE, "sequence %d is swapped out", parent);
     if (n_shared < 0 || n_shared > s->len)
         return fail(PKV_ERR_INVALID_ARG, "fork length %d must be in [0, parent length %d]", n_shared, s->len);
     if (p->next_id == std::numeric_limits<int32_t>::max()) return fail(PKV_ERR_OUT_OF_RANGE, "sequence ids exhausted");
@@ -511,6 +520,7 @@ int kv_block_tables(const kv_pool_t* p, const int32_t* seqs, int32_t n, int32_t 
     for (int32_t i = 0; i < n; ++i) {
         const Seq* s = find_seq(p, seqs[i]);
         if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seqs[i]);
+        if (s->swapped) return fail(PKV_ERR_STATE, "sequence %d is swapped out", seqs[i]);
         if ((int64_t)s->blocks.size() > max_blocks)
             return fail(PKV_ERR_OUT_OF_RANGE, "sequence %d has %zu blocks > max_blocks_per_seq %d", seqs[i],
                         s->blocks.size(), max_blocks);
@@ -564,6 +574,7 @@ int kv_prefix_register(kv_pool_t* p, int32_t seq, const int32_t* tokens, int32_t
     if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
     const Seq* s = find_seq(p, seq);
     if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
+    if (s->swapped) return fail(PKV_ERR_STATE, "sequence %d is swapped out", seq);
     if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return fail(PKV_ERR_INVALID_ARG, "bad token array");
     if (n_tokens > s->len) return fail(PKV_ERR_OUT_OF_RANGE, "%d tokens given, sequence holds %d", n_tokens, s->len);
     const int bs = p->block_size;
@@ -947,6 +958,133 @@ int paged_prefill(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t n_seqs, 
     if (rc != PKV_OK) return rc;
     hipError_t e = timed_launch(p, "paged_prefill", s, [&] { return pkv::launch_prefill(d, max_q_len, s); });
     if (e != hipSuccess) return hip_fail(e, "paged_prefill launch");
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device staging of at least `bytes` for a swap (the pool keeps the largest so far).
+int ensure_staging(kv_pool* p, size_t bytes) {
+    if (p->staging_bytes >= bytes) return PKV_OK;
+    if (p->staging) {
+        hipError_t e = hipFree(p->staging);
+        p->staging = nullptr;
+        p->staging_bytes = 0;
+        if (e != hipSuccess) return hip_fail(e, "staging release");
+    }
+    hipError_t e = hipMalloc(&p->staging, bytes);
+    if (e != hipSuccess) {
+        p->staging = nullptr;
+        return hip_fail(e, "swap staging allocation");
+    }
+    p->staging_bytes = bytes;
+    return PKV_OK;
+}
+
+// Move the blocks `ids` (logical order) between the pools and the staging buffer.
+hipError_t move_blocks(kv_pool* p, const std::vector<int32_t>& ids, bool to_pool, hipStream_t s) {
+    pkv::MoveParams mp{};
+    mp.k_pool = p->k_pool;
+    mp.v_pool = p->v_pool;
+    mp.staging = reinterpret_cast<char*>(p->staging);
+    mp.block_bytes = (int64_t)p->kv_heads * p->block_bytes;    // a whole block: every KV head's tile
+    mp.to_pool = to_pool ? 1 : 0;
+    for (size_t i = 0; i < ids.size(); i += pkv::kMaxCopiesPerLaunch) {
+        const size_t n = std::min<size_t>(pkv::kMaxCopiesPerLaunch, ids.size() - i);
+        for (size_t k = 0; k < n; ++k) mp.ids[k] = ids[i + k];
+        mp.n = (int32_t)n;
+        mp.first = (int64_t)i;
+        hipError_t e = pkv::launch_move_blocks(mp, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+size_t swap_bytes_of(const kv_pool* p, int32_t len) {
+    return (size_t)((len + p->block_size - 1) / p->block_size) * 2 * p->kv_heads * p->block_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_seq_swap_bytes(const kv_pool_t* p, int32_t seq, size_t* bytes) {
+    if (!p || !bytes) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+    const Seq* s = find_seq(p, seq);
+    if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
+    *bytes = swap_bytes_of(p, s->len);
+    return ok();
+}
+
+int kv_seq_swap_out(kv_pool_t* p, int32_t seq, void* host_dst, size_t bytes, void* stream) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    Seq* s = find_seq(p, seq);
+    if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
+    if (s->swapped) return fail(PKV_ERR_STATE, "sequence %d is already swapped out", seq);
+    const size_t need = swap_bytes_of(p, s->len);
+    if (!p->host_only && bytes < need)
+        return fail(PKV_ERR_INVALID_ARG, "swap buffer of %zu bytes, %zu needed", bytes, need);
+    if (need > 0 && !host_dst && !p->host_only) return fail(PKV_ERR_INVALID_ARG, "host_dst is NULL");
+    if (need > 0 && !p->host_only) {
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        int rc = flush_copies(p, st);                  // the blocks may be owed a copy
+        if (rc == PKV_OK) rc = ensure_staging(p, need);
+        if (rc != PKV_OK) return rc;
+        hipError_t e = move_blocks(p, s->blocks, false, st);
+        if (e == hipSuccess) e = hipMemcpyAsync(host_dst, p->staging, need, hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "swap-out copy");
+    }
+    for (auto b = s->blocks.rbegin(); b != s->blocks.rend(); ++b) {   // as kv_seq_free: deepest first
+        ref_dec(p, *b);
+        if (p->ref[*b] == 0) release_block(p, *b);
+    }
+    s->blocks.clear();
+    s->swapped = true;
+    return ok();
+}
+
+int kv_seq_swap_in(kv_pool_t* p, int32_t seq, const void* host_src, size_t bytes, void* stream) {
+    if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+    Seq* s = find_seq(p, seq);
+    if (!s) return fail(PKV_ERR_STATE, "unknown or freed sequence %d", seq);
+    if (!s->swapped) return fail(PKV_ERR_STATE, "sequence %d is not swapped out", seq);
+    const size_t need = swap_bytes_of(p, s->len);
+    if (!p->host_only && bytes < need)
+        return fail(PKV_ERR_INVALID_ARG, "swap buffer of %zu bytes, %zu needed", bytes, need);
+    if (need > 0 && !host_src && !p->host_only) return fail(PKV_ERR_INVALID_ARG, "host_src is NULL");
+    const size_t nb = (size_t)((s->len + p->block_size - 1) / p->block_size);
+    if (nb > available(p)) return fail(PKV_ERR_NO_BLOCKS, "swap-in needs %zu blocks, %zu available", nb, available(p));
+    std::vector<int32_t> blocks;
+    try {
+        blocks.reserve(nb);
+    } catch (...) {
+        return fail(PKV_ERR_DEVICE, "host allocation failed");
+    }
+    for (size_t i = 0; i < nb; ++i) blocks.push_back(take_block(p));
+    if (need > 0 && !p->host_only) {
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        int rc = flush_copies(p, st);
+        if (rc == PKV_OK) rc = ensure_staging(p, need);
+        hipError_t e = hipSuccess;
+        if (rc == PKV_OK) {
+            e = hipMemcpyAsync(p->staging, host_src, need, hipMemcpyHostToDevice, st);
+            if (e == hipSuccess) e = move_blocks(p, blocks, true, st);
+            if (e == hipSuccess) e = hipStreamSynchronize(st);
+            if (e != hipSuccess) rc = hip_fail(e, "swap-in copy");
+        }
+        if (rc != PKV_OK) {                            // give the blocks back; the sequence stays out
+            for (auto b = blocks.rbegin(); b != blocks.rend(); ++b) {
+                ref_dec(p, *b);
+                if (p->ref[*b] == 0) release_block(p, *b);
+            }
+            return rc;
+        }
+    }
+    s->blocks = std::move(blocks);
+    s->swapped = false;
     return ok();
 }
 

@@ -60,11 +60,14 @@ def _compare(pool, model, live):
     assert list(pool.free_list()) == model.free_list()
     for b in range(model.N):
         assert pool.block_refcount(b) == model.refcount(b)
-    if live:
-        mb = max(1, max(len(model.table(s)) for s in live))
-        t, l = pool.block_tables(live, mb)
-        mt, ml = model.tables(live, mb)
+    resident = [s for s in live if s not in model.swapped]
+    if resident:
+        mb = max(1, max(len(model.table(s)) for s in resident))
+        t, l = pool.block_tables(resident, mb)
+        mt, ml = model.tables(resident, mb)
         assert np.array_equal(t, np.array(mt, np.int32)) and list(l) == ml
+    for s in live:
+        assert pool.seq_length(s) == model.length(s)
     info = pool.info()
     assert info["free_blocks"] == len(model.free_list())
     assert info["shared_blocks"] == model.shared_blocks()
@@ -94,16 +97,34 @@ def test_allocator_matches_model_on_random_traces(seed):
     model = BlockPoolModel(n, 16, free_order=order)
     live = []
     _TOKS.clear()
-    hits = evicted = 0
+    hits = evicted = swaps = 0
     for step in range(800):
         cached_before = len(model.cache)
-        op = int(rng.integers(0, 8))
-        if op == 5 and live:                            # publish a sequence's blocks
-            s = live[int(rng.integers(len(live)))]
+        op = int(rng.integers(0, 10))
+        resident = [x for x in live if x not in model.swapped]
+        if op == 8 and resident:                        # swap a sequence out (no data on this pool)
+            s = resident[int(rng.integers(len(resident)))]
+            model.swap_out(s)
+            assert pool.swap_out(s) is None
+            swaps += 1
+        elif op == 9 and model.swapped & set(live):     # and back in
+            s = sorted(model.swapped & set(live))[int(rng.integers(len(model.swapped & set(live))))]
+            try:
+                model.swap_in(s)
+            except AllocError as e:
+                with pytest.raises(pkv.PagedKVError) as got:
+                    pool.swap_in(s)
+                assert got.value.code == MAP[e.code]
+            else:
+                pool.swap_in(s)
+        elif op in (5, 6, 3) and not resident:
+            pass
+        elif op == 5 and live:                          # publish a sequence's blocks
+            s = resident[int(rng.integers(len(resident)))]
             toks = _tokens(s, model.length(s))
             assert pool.prefix_register(s, toks, ns=s % 3) == model.prefix_register(s, toks, ns=s % 3)
         elif op == 6 and live:                          # a request reusing a cached prefix
-            s = live[int(rng.integers(len(live)))]
+            s = resident[int(rng.integers(len(resident)))]
             toks = _tokens(s, model.length(s)) + [7] * int(rng.integers(0, 20))
             a, b = pool.seq_create_cached(toks, ns=s % 3), model.seq_create_cached(toks, ns=s % 3)
             assert a == b
@@ -130,7 +151,7 @@ def test_allocator_matches_model_on_random_traces(seed):
                 assert list(pool.seq_reserve(s, k)) == want
             assert pool.seq_length(s) == model.length(s)
         elif op == 3:
-            p = live[int(rng.integers(len(live)))]
+            p = resident[int(rng.integers(len(resident)))]
             k = int(rng.integers(0, model.length(p) + 1))      # any length: partial blocks shared
             a, b = pool.seq_fork(p, k), model.fork(p, k)
             assert a == b
@@ -150,8 +171,8 @@ def test_allocator_matches_model_on_random_traces(seed):
     _compare(pool, model, live)
     assert pool.pending_copies() == model.take_copies()
     pool.close()
-    print(f"seed {seed}: {hits} cached blocks reused, {evicted} evicted by allocation")
-    assert hits > 0
+    print(f"seed {seed}: {hits} cached blocks reused, {evicted} evicted by allocation, {swaps} swaps")
+    assert hits > 0 and swaps > 0
 
 
 def test_allocator_errors():

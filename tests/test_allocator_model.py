@@ -190,3 +190,47 @@ def test_prefix_cache_never_shares_on_a_hash_match_alone():
     m.key_of[m.table(a)[0]] = (key, [999] * 16)         # plant stored tokens that differ
     _, hit = m.seq_create_cached(list(range(16)))
     assert hit == 0
+
+
+def test_swap_out_and_in():
+    # cf-1.com/news/5824798 §2.2: inactive blocks may move to host memory and come
+    # back on demand; here a whole sequence at a time
+    m = BlockPoolModel(8, 16, free_order=range(8))
+    a = m.seq_create()
+    m.reserve(a, 40)                                  # blocks 0, 1, 2
+    b = m.fork(a, 32)                                 # shares 0, 1
+    assert m.swap_out(a) == 3
+    assert m.free_list() == [3, 4, 5, 6, 7, 2]        # only its private block came free
+    assert m.refcount(0) == 1 and m.length(a) == 40
+    for op in (lambda: m.reserve(a, 1), lambda: m.fork(a, 1), lambda: m.table(a), lambda: m.swap_out(a)):
+        with pytest.raises(AllocError) as e:
+            op()
+        assert e.value.code == STATE
+    assert m.swap_in(a) == [3, 4, 5]                  # fresh private copies, logical order
+    assert m.table(b) == [0, 1] and m.refcount(0) == 1
+    m.reserve(a, 9)                                   # grows normally afterwards
+    assert m.table(a) == [3, 4, 5, 6]
+    with pytest.raises(AllocError) as e:
+        m.swap_in(a)                                  # not swapped out
+    assert e.value.code == STATE
+    c = m.seq_create()
+    m.reserve(c, 32)                                  # the last two free blocks
+    assert m.table(c) == [7, 2] and m.free_list() == []
+    m.check_invariants()
+
+
+def test_swap_in_is_all_or_nothing():
+    m = BlockPoolModel(4, 16)
+    a = m.seq_create()
+    m.reserve(a, 64)
+    m.swap_out(a)
+    b = m.seq_create()
+    m.reserve(b, 16)                                  # one of the four blocks is taken
+    before = m.free_list()
+    with pytest.raises(AllocError) as e:
+        m.swap_in(a)
+    assert e.value.code == NO_BLOCKS and m.free_list() == before and a in m.swapped
+    m.free_seq(b)
+    assert len(m.swap_in(a)) == 4
+    m.free_seq(a)                                     # a swapped or resident sequence frees alike
+    m.check_invariants()
