@@ -275,12 +275,57 @@ def cpu_baseline_prefill(w, budget_s: float = 15.0):
                       f"the same algorithmic flops per row as value"}
 
 
+SWAP_METRIC = "sequence swap-out + swap-in GB/s (host <-> HBM, pinned), 1 MI355X"
+
+
+def bench_swap(args):
+    """Swap one long sequence out to pinned host memory and back, K times.
+    value = bytes moved (out + in) / time of the pair.  Each call is
+    synchronous, so host wall time brackets it."""
+    import torch
+    import harness
+    import paged_kv_cache_152_amd as pkv
+    H_kv, D, n = 8, 128, 32768                       # one Llama-3-8B-shaped layer, 32K context, bf16
+    nb = -(-n // wl.BLOCK)
+    pool = pkv.KVPool(nb + 8, H_kv, D, pkv.BF16, free_order=np.random.default_rng(8).permutation(nb + 8))
+    s = pool.seq_create()
+    slots = torch.from_numpy(pool.seq_reserve(s, n)).cuda()
+    kv = torch.randn(n, H_kv, D, device="cuda").to(torch.bfloat16)
+    pool.append(slots, kv, kv)
+    torch.cuda.synchronize()
+    nbytes = pool.swap_bytes(s)
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    for _ in range(args.warmup):
+        pool.swap_out(s, host)
+        pool.swap_in(s, host)
+    t_out = t_in = 0.0
+    for _ in range(args.steps):
+        t0 = time.perf_counter()
+        pool.swap_out(s, host)
+        t1 = time.perf_counter()
+        pool.swap_in(s, host)
+        t2 = time.perf_counter()
+        t_out += t1 - t0
+        t_in += t2 - t1
+    pool.close()
+    step = (t_out + t_in) / args.steps
+    result = {"metric": SWAP_METRIC, "value": round(2 * nbytes / step / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+              "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step * 1e3, 4),
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic (random bf16 K/V)",
+              "config": {"workload": "swap", "kv_heads": H_kv, "head_dim": D, "tokens": n, "bytes_each_way": nbytes},
+              "swap_out_GBps": round(nbytes * args.steps / t_out / 1e9, 2),
+              "swap_in_GBps": round(nbytes * args.steps / t_in / 1e9, 2),
+              "roofline": None, "cpu_baseline": None}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8", "prefill8b"])
+    ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8", "prefill8b", "swap"])
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -292,6 +337,8 @@ def main():
 
     if args.workload.startswith("prefill"):
         return bench_prefill(args)
+    if args.workload == "swap":
+        return bench_swap(args)
 
     import torch
     import harness
