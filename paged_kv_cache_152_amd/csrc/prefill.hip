@@ -87,6 +87,17 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
     else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
+// The sum of the two 16-bit values of type PT packed in w, in fp32 (exact widening).
+template <int PT>
+__device__ __forceinline__ float sum2(uint32_t w) {
+    if constexpr (PT == DT_BF16)
+        return __builtin_bit_cast(float, w << 16) + __builtin_bit_cast(float, w & 0xffff0000u);
+    else {
+        const f16x2_t h = __builtin_bit_cast(f16x2_t, w);
+        return (float)h[0] + (float)h[1];
+    }
+}
+
 // 8 E4M3 codes -> 8 values of 16-bit type T, exact.
 template <int T>
 __device__ __forceinline__ uint4 fp8x8_to(uint2 w) {
@@ -150,11 +161,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillPar
     constexpr int KT = KDT == DT_FP8 ? QDT : KDT;            // type of K in Q.K^T
     constexpr int KE = KDT == DT_FP8 ? 1 : 2;  // bytes per stored K/V element
     constexpr int EPL = D / 16;                // elements of a tile one thread stages (16 threads a token)
-    constexpr int KROW = D + 8;                // LDS K row, padded (16-bit elements)
-    constexpr int VROW = 20;                   // LDS V^T row: 16 tokens + padding
+    constexpr int KROW = D + 8;                // LDS row of a K or V tile, padded (16-bit elements)
+    constexpr float kLazy = 8.0f;              // a row's reference max moves only when exceeded by 2^8
     using QV = typename Vec8<QDT>::T;
     __shared__ __align__(16) uint16_t ks_lds[2][16 * KROW];
-    __shared__ __align__(16) uint16_t vt_lds[2][D * VROW];
+    __shared__ __align__(16) uint16_t vs_lds[2][16 * KROW];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane >> 4, c = lane & 15;
@@ -235,57 +246,53 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillPar
         st.k = *reinterpret_cast<const Raw*>(kbase + off);
         st.v = *reinterpret_cast<const Raw*>(vbase + off);
     };
-    // K tile natural ([token][dim], K's MFMA type), V tile transposed ([dim][token], PT); dead rows zero
+    // K tile in K's MFMA type, V tile in PT, both [token][dim] as stored; dead rows zero
     auto stage = [&](int j, const Stage& st, int buf) {
         const bool ok = st.ok && j * kBlock + st_tok < n;
-        uint16_t ke[EPL], ve[EPL];
+        uint16_t* kd = &ks_lds[buf][st_tok * KROW + st_el];
+        uint16_t* vd = &vs_lds[buf][st_tok * KROW + st_el];
         if constexpr (KDT == DT_FP8) {
             if constexpr (EPL == 8) {
-                const uint4 kw = fp8x8_to<KT>(*reinterpret_cast<const uint2*>(&st.k));
-                const uint4 vw = fp8x8_to<DT_F16>(*reinterpret_cast<const uint2*>(&st.v));
-                const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ke[2 * e] = (uint16_t)kk[e]; ke[2 * e + 1] = (uint16_t)(kk[e] >> 16);
-                    ve[2 * e] = (uint16_t)vv[e]; ve[2 * e + 1] = (uint16_t)(vv[e] >> 16);
-                }
+                uint4 kw = fp8x8_to<KT>(*reinterpret_cast<const uint2*>(&st.k));
+                uint4 vw = fp8x8_to<DT_F16>(*reinterpret_cast<const uint2*>(&st.v));
+                if (!ok) kw = vw = make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4*>(kd) = kw;
+                *reinterpret_cast<uint4*>(vd) = vw;
             } else {
                 const uint32_t kc = *reinterpret_cast<const uint32_t*>(&st.k);
                 const uint32_t vc = *reinterpret_cast<const uint32_t*>(&st.v);
-                uint32_t kk[2], vv[2];
+                uint2 kw, vw;
                 if constexpr (KT == DT_BF16) {
-                    kk[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kc, 1.0f, false));
-                    kk[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kc, 1.0f, true));
+                    kw.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kc, 1.0f, false));
+                    kw.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kc, 1.0f, true));
                 } else {
-                    kk[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kc, 1.0f, false));
-                    kk[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kc, 1.0f, true));
+                    kw.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kc, 1.0f, false));
+                    kw.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kc, 1.0f, true));
                 }
-                vv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vc, 1.0f, false));
-                vv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vc, 1.0f, true));
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    ke[2 * e] = (uint16_t)kk[e]; ke[2 * e + 1] = (uint16_t)(kk[e] >> 16);
-                    ve[2 * e] = (uint16_t)vv[e]; ve[2 * e + 1] = (uint16_t)(vv[e] >> 16);
-                }
+                vw.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vc, 1.0f, false));
+                vw.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vc, 1.0f, true));
+                if (!ok) kw = vw = make_uint2(0u, 0u);
+                *reinterpret_cast<uint2*>(kd) = kw;
+                *reinterpret_cast<uint2*>(vd) = vw;
             }
         } else {
+            constexpr int NW = sizeof(Raw) / 4;
             const uint32_t* kw = reinterpret_cast<const uint32_t*>(&st.k);
             const uint32_t* vw = reinterpret_cast<const uint32_t*>(&st.v);
+            uint32_t kz[NW], vz[NW];
 #pragma unroll
-            for (int e = 0; e < EPL / 2; ++e) {
-                ke[2 * e] = (uint16_t)kw[e]; ke[2 * e + 1] = (uint16_t)(kw[e] >> 16);
-                ve[2 * e] = (uint16_t)vw[e]; ve[2 * e + 1] = (uint16_t)(vw[e] >> 16);
+            for (int w = 0; w < NW; ++w) {
+                kz[w] = ok ? kw[w] : 0u;
+                vz[w] = ok ? vw[w] : 0u;
+            }
+            if constexpr (NW == 4) {
+                *reinterpret_cast<uint4*>(kd) = make_uint4(kz[0], kz[1], kz[2], kz[3]);
+                *reinterpret_cast<uint4*>(vd) = make_uint4(vz[0], vz[1], vz[2], vz[3]);
+            } else {
+                *reinterpret_cast<uint2*>(kd) = make_uint2(kz[0], kz[1]);
+                *reinterpret_cast<uint2*>(vd) = make_uint2(vz[0], vz[1]);
             }
         }
-        uint32_t kp[EPL / 2];
-#pragma unroll
-        for (int e = 0; e < EPL / 2; ++e)
-            kp[e] = ok ? (uint32_t)ke[2 * e] | ((uint32_t)ke[2 * e + 1] << 16) : 0u;
-        uint16_t* kd = &ks_lds[buf][st_tok * KROW + st_el];
-        if constexpr (EPL == 8) *reinterpret_cast<uint4*>(kd) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
-        else *reinterpret_cast<uint2*>(kd) = make_uint2(kp[0], kp[1]);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vt_lds[buf][(st_el + e) * VROW + st_tok] = ok ? ve[e] : (uint16_t)0;
     };
 
     f32x4_t acc[R][MT];
@@ -298,7 +305,13 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillPar
         for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    auto compute = [&](int j, int buf) {
+    // Rows keep a reference max m_ref that moves only when a logit exceeds it
+    // by more than 2^kLazy: the weights exp2(z - m_ref) stay <= 2^kLazy (exact
+    // in fp32, the same relative precision in 16-bit), and the accumulators are
+    // rescaled only on those moves.  A block every live row sees in full takes
+    // the unmasked path.
+    const int wg_min_see = p.causal ? n - q_len + tile0 : n - 1;
+    auto compute = [&](bool masked, int j, int buf) {
         // K operand (token c, dims 32 k + 8 r), shared by the row groups
         typename Vec8<KT>::T ka[KS];
 #pragma unroll
@@ -314,27 +327,37 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillPar
             float z[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool vis = live[rg] && tok + i < n && tok + i <= see[rg];
+                const bool vis = live[rg] && (!masked || (tok + i < n && tok + i <= see[rg]));
                 z[i] = vis ? S[i] * qscale : -INFINITY;      // select, never 0 * garbage
             }
             const float m_blk = across_rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-            const float m_new = fmaxf(m_run[rg], m_blk);
-            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[rg] - m_use);
+            if (__builtin_amdgcn_ballot_w64(m_blk > m_run[rg] + kLazy) != 0) {
+                const float m_new = m_blk > m_run[rg] + kLazy ? m_blk : m_run[rg];
+                const float alpha = m_new == m_run[rg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
+                l_run[rg] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[rg][mt] *= alpha;
+                m_run[rg] = m_new;
+            }
+            const float m_use = m_run[rg] == -INFINITY ? 0.0f : m_run[rg];
             float pr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_use);
-            l_run[rg] = fmaf(l_run[rg], alpha, across_rows_sum((pr[0] + pr[1]) + (pr[2] + pr[3])));
-            m_run[rg] = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[rg][mt] *= alpha;
-            }
+            // l sums the rounded weights P.V multiplies, so the output is a normalised
+            // average of those weights and a row's dominant weight carries no rounding
             pb[rg] = make_uint2(pack2<PT>(pr[0], pr[1]), pack2<PT>(pr[2], pr[3]));
+            l_run[rg] += across_rows_sum(sum2<PT>(pb[rg].x) + sum2<PT>(pb[rg].y));
         }
+        // V^T operand: dim 16 mt + c, tokens 4 r .. 4 r + 3.  ds_read_b64_tr_b16
+        // builds, in each 16-lane group, row k from the 4 elements lanes 4k ..
+        // 4k + 3 point at and hands lane i element i of rows 0 .. 3; so lane
+        // (r, c) points at token 4 r + c / 4, dims 16 mt + 4 (c % 4) .. + 3.
+        const uint16_t* vsrc = &vs_lds[buf][(4 * r + (c >> 2)) * KROW + 4 * (c & 3)];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const uint2 va = *reinterpret_cast<const uint2*>(&vt_lds[buf][(16 * mt + c) * VROW + 4 * r]);
+            const uint2 va = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (__attribute__((address_space(3))) s16x4_t*)(vsrc + 16 * mt)));
 #pragma unroll
             for (int rg = 0; rg < R; ++rg) acc[rg][mt] = mma_k16<PT>(va, pb[rg], acc[rg][mt]);
         }
@@ -353,7 +376,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillPar
                 stage(j, ring[k], j & 1);
                 if (j + kAhead < nblk) fetch(j + kAhead, ring[k]);
                 __syncthreads();                             // tiles of block j are in LDS
-                compute(j, j & 1);
+                compute(!((j + 1) * kBlock <= n && j * kBlock + kBlock - 1 <= wg_min_see), j, j & 1);
             }
         }
     }
