@@ -67,7 +67,7 @@ typedef struct {
     float* v_scale;            /* device; [kv_heads] (FP8 pools only, else NULL) */
     uint64_t pool_bytes;       /* bytes of ONE of k_pool / v_pool */
     uint64_t block_bytes;      /* bytes of one (block, kv head) tile = block_size*head_dim*elem */
-    uint64_t total_bytes;      /* device bytes owned: 2*pool_bytes + scales */
+    uint64_t total_bytes;      /* device bytes owned: 2*pool_bytes + scales + a 4 KiB zero tile */
     int32_t num_blocks, block_size, kv_heads, head_dim, dtype, elem_bytes;
     int32_t free_blocks;       /* refcount 0 */
     int32_t used_blocks;       /* refcount >= 1 */

@@ -9,6 +9,7 @@
 namespace pkv {
 
 constexpr int kBlock = 16;        // tokens per physical block
+constexpr int kZeroTileBytes = kBlock * 128 * 2;   // one 16-token tile of the widest 16-bit row
 constexpr int kDecodeWaves = 4;   // waves per decode workgroup
 constexpr int kMaxGroupPerWg = 8; // query heads one decode workgroup serves
 
@@ -88,6 +89,7 @@ struct PrefillParams {
     const int32_t* q_start;   // [n_seqs + 1]
     const int32_t* tables;    // [n_seqs][max_blocks]
     const int32_t* lens;      // [n_seqs] context lengths including the chunk
+    const void* zero_tile;    // kZeroTileBytes of zeros: the source of absent tokens
     int32_t n_seqs, total_q, H_q, H_kv, G, D, num_blocks, max_blocks;
     int32_t gs;               // query heads per row group (divides G, at most 16)
     int64_t tiles;            // query tiles per (sequence, head group), set by the launcher

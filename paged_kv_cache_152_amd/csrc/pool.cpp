@@ -75,6 +75,7 @@ struct kv_pool {
     void* k_pool = nullptr;
     void* v_pool = nullptr;
     float* scales = nullptr;   // device: k_scale[H], v_scale[H], k_inv[H], v_inv[H]
+    void* zero_tile = nullptr; // device: kZeroTileBytes of zeros (paged_prefill reads absent tokens here)
     uint64_t pool_bytes = 0, block_bytes = 0;
     int32_t partition_tokens = 0;
 
@@ -194,6 +195,8 @@ int create_common(int32_t num_blocks, int32_t block_size, int32_t kv_heads, int3
         if (e == hipSuccess) e = hipMalloc(&p->v_pool, p->pool_bytes);
         if (e == hipSuccess) e = hipMemset(p->k_pool, 0, p->pool_bytes);
         if (e == hipSuccess) e = hipMemset(p->v_pool, 0, p->pool_bytes);
+        if (e == hipSuccess) e = hipMalloc(&p->zero_tile, pkv::kZeroTileBytes);
+        if (e == hipSuccess) e = hipMemset(p->zero_tile, 0, pkv::kZeroTileBytes);
         if (e == hipSuccess && dtype == PKV_FP8_E4M3) {
             e = hipMalloc(&p->scales, sizeof(float) * 4 * kv_heads);
             if (e == hipSuccess) {
@@ -309,6 +312,7 @@ int kv_pool_destroy(kv_pool_t* pool) {
         if (pool->k_pool) hipFree(pool->k_pool);
         if (pool->v_pool) hipFree(pool->v_pool);
         if (pool->scales) hipFree(pool->scales);
+        if (pool->zero_tile) hipFree(pool->zero_tile);
         if (pool->staging) hipFree(pool->staging);
     }
     delete pool;
@@ -324,7 +328,9 @@ int kv_pool_info(const kv_pool_t* p, kv_pool_info_t* out) {
     out->v_scale = p->scales ? p->scales + p->kv_heads : nullptr;
     out->pool_bytes = p->pool_bytes;
     out->block_bytes = p->block_bytes;
-    out->total_bytes = p->host_only ? 0 : 2 * p->pool_bytes + (p->scales ? 4ull * sizeof(float) * p->kv_heads : 0);
+    out->total_bytes = p->host_only ? 0
+                                    : 2 * p->pool_bytes + (p->scales ? 4ull * sizeof(float) * p->kv_heads : 0) +
+                                          (uint64_t)pkv::kZeroTileBytes;
     out->num_blocks = p->num_blocks;
     out->block_size = p->block_size;
     out->kv_heads = p->kv_heads;
@@ -940,6 +946,7 @@ int paged_prefill(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t n_seqs, 
     d.q_start = q_start;
     d.tables = block_tables;
     d.lens = context_lens;
+    d.zero_tile = p->zero_tile;
     d.n_seqs = n_seqs;
     d.total_q = total_q;
     d.H_q = H_q;

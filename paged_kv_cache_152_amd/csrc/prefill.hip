@@ -399,6 +399,267 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillPar
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit pools: K and V go from HBM straight into LDS (global_load_lds_dwordx4,
+// no registers on the way), kStages stages of 32 tokens (two blocks) in
+// flight.  A stage row is one token's head_dim values; its 16-byte chunks are
+// XOR-swizzled by row so that the K-operand reads (16 rows, one chunk each)
+// and the transposed V reads (4 rows x 32 bytes per 16 lanes) hit distinct
+// banks.  Tokens past the context and blocks outside the pool load from a
+// zero tile instead, so no stored garbage reaches P.V.
+//
+// Per 32-token stage, for each row group: S^T of the two blocks on
+// 2 x head_dim / 32 v_mfma_f32_16x16x32; the lane then holds the weights of
+// tokens 4 (l / 16) .. +3 of both blocks for row l % 16, which is the B layout
+// of a 16x16x32 product with k = 8 (l / 16) + i standing for those 8 tokens.
+// O^T += V^T . P^T on head_dim / 16 v_mfma_f32_16x16x32, A built from two
+// ds_read_b64_tr_b16 (one per block) in the same token order.
+constexpr int kStages = 4;
+
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+    if constexpr (D == 128) return row & 15;       // 16 chunks a row: rows 0..15 spread over all banks
+    else return (row >> 1) & 7;                    // 8 chunks a row: two rows per bank sweep
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding,
+// then meet the other waves.  Written as one asm statement with a memory
+// clobber: the compiler neither moves LDS accesses across it nor adds a full
+// drain of the LDS-bound loads, as a fenced barrier would.
+template <int N>
+__device__ __forceinline__ void wait_loads_then_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// A wave-uniform 32-bit read through the scalar cache.  The compiler would
+// issue it as a vector load inside the stage loop (it cannot prove the table
+// unclobbered by the LDS-bound loads) and then drain the vector counter.
+__device__ __forceinline__ int32_t scalar_read(const int32_t* ptr) {
+    int32_t v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+    return v;
+}
+
+template <int KDT, int D>
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill_dma_kernel(PrefillParams p) {
+    constexpr int QDT = KDT;
+    constexpr int KS = D / 32;                 // S^T steps per block (32 dims each)
+    constexpr int MT = D / 16;                 // O^T m-tiles (16 dims each)
+    constexpr int R = kRowGroups;
+    constexpr int ROWB = D * 2;                // bytes of a token row
+    constexpr int CH = ROWB / 16;              // 16-byte chunks per row
+    constexpr int SROWS = 2 * kBlock;          // token rows per stage
+    constexpr int NI = SROWS * CH / (64 * kPfWaves);   // loads per wave per tensor per stage
+    constexpr int LPS = 2 * NI;                // loads per wave per stage (K and V)
+    constexpr int SE = SROWS * D;              // 16-bit elements of one tensor's stage
+    constexpr float kLazy = 8.0f;
+    static_assert(NI >= 1 && (64 / CH) * NI * kPfWaves == SROWS, "stage rows split evenly over the loads");
+    using QV = typename Vec8<QDT>::T;
+    typedef __attribute__((address_space(3))) void lds_void;
+    __shared__ __align__(16) uint16_t k_lds[kStages][SE];
+    __shared__ __align__(16) uint16_t v_lds[kStages][SE];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane >> 4, c = lane & 15;
+    const int gs = p.gs, subs = p.G / gs;
+    const int tw = (16 * R) / gs;                            // query tokens per wave
+    const int64_t tiles = p.tiles;
+    const int64_t n_wg = tiles * p.H_kv * subs * p.n_seqs;
+    const int64_t L = xcd_logical(blockIdx.x, n_wg);
+    const int tile = (int)(L % tiles);
+    const int hgi = (int)((L / tiles) % ((int64_t)p.H_kv * subs));
+    const int s = (int)(L / (tiles * p.H_kv * subs));
+    const int g = hgi / subs;
+    const int hq0 = g * p.G + (hgi % subs) * gs;
+
+    const int q0 = min(p.q_start[s], p.total_q), q1 = min(max(p.q_start[s + 1], q0), p.total_q);
+    const int q_len = q1 - q0;
+    int n = p.lens[s];
+    n = n < 0 ? 0 : (n > p.max_blocks * kBlock ? p.max_blocks * kBlock : n);
+    const int tile0 = tile * kPfWaves * tw;                 // first query token of the workgroup
+    if (tile0 >= q_len) return;
+    const int tile_last = min(q_len, tile0 + kPfWaves * tw) - 1;
+    const int wg_see = p.causal ? n - q_len + tile_last : n - 1;
+    const int nblk = wg_see < 0 ? 0 : min((wg_see + kBlock) / kBlock, (n + kBlock - 1) / kBlock);
+    const int n_it = (nblk + 1) >> 1;
+
+    // A negative scale flips q's sign bits (exact) so that the logit scale is
+    // positive and the row max can be taken before scaling.
+    const float scale2 = p.scale * kLog2e;
+    const uint32_t qflip = scale2 < 0.0f ? 0x80008000u : 0u;
+    const float qscale = fmaxf(fabsf(scale2), 1e-30f);
+
+    int see[R];
+    bool live[R];
+    int i_row[R];
+    QV qb[R][KS];
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q);
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) {
+        const int row = rg * 16 + c;
+        i_row[rg] = tile0 + wave * tw + row / gs;
+        live[rg] = row < tw * gs && i_row[rg] < q_len;
+        see[rg] = p.causal ? n - q_len + i_row[rg] : n - 1;
+        const int64_t qrow = ((int64_t)(q0 + i_row[rg]) * p.H_q + hq0 + row % gs) * D;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+            if (live[rg]) raw = *reinterpret_cast<const uint4*>(q16 + qrow + 32 * k + 8 * r);
+            raw.x ^= qflip; raw.y ^= qflip; raw.z ^= qflip; raw.w ^= qflip;
+            qb[rg][k] = __builtin_bit_cast(QV, raw);
+        }
+    }
+
+    // Load geometry: load i of this wave fills stage chunks (wave * NI + i) * 64
+    // + lane, i.e. row ld_row, physical chunk lane % CH, holding logical chunk
+    // (lane % CH) ^ swizzle(row).  All rows of one load lie in one block.
+    const int32_t* table = p.tables + (int64_t)s * p.max_blocks;
+    const char* kbase = reinterpret_cast<const char*>(p.k_pool) + (int64_t)g * kBlock * ROWB;
+    const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (int64_t)g * kBlock * ROWB;
+    const char* zero = reinterpret_cast<const char*>(p.zero_tile);
+    const int64_t blk_stride = (int64_t)p.H_kv * kBlock * ROWB;
+    int ld_row[NI], ld_off[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int slot = (wave * NI + i) * 64 + lane;
+        const int row = slot / CH, pch = slot % CH;
+        ld_row[i] = row;
+        ld_off[i] = (row % kBlock) * ROWB + ((pch ^ chunk_swizzle<D>(row)) * 16);
+    }
+    auto issue = [&](int jj) {                 // the loads of stage jj (blocks 2 jj, 2 jj + 1)
+        // wave-uniform table reads: scalar loads, which do not count against the
+        // vector-memory counter the stage waits use
+        const int ph0 = scalar_read(table + 2 * jj);
+        const int ph1 = 2 * jj + 1 < nblk ? scalar_read(table + 2 * jj + 1) : -1;
+        const int buf = jj % kStages;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int row = ld_row[i];
+            const int ph = row >= kBlock ? ph1 : ph0;
+            const bool ok = ph >= 0 && ph < p.num_blocks && 2 * jj * kBlock + row < n;
+            const int64_t off = (int64_t)ph * blk_stride + ld_off[i];
+            const char* ks = ok ? kbase + off : zero + ld_off[i];
+            const char* vs = ok ? vbase + off : zero + ld_off[i];
+            const int dst = (wave * NI + i) * 64 * 8;          // 16-bit elements
+            __builtin_amdgcn_global_load_lds(ks, (lds_void*)&k_lds[buf][dst], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vs, (lds_void*)&v_lds[buf][dst], 16, 0, 0);
+        }
+    };
+
+    f32x4_t acc[R][MT];
+    float m_run[R], l_run[R];
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) {
+        m_run[rg] = -INFINITY;
+        l_run[rg] = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    const int wg_min_see = p.causal ? n - q_len + tile0 : n - 1;
+    auto compute = [&](bool masked, int j, int buf) {
+        const uint16_t* kt = k_lds[buf];
+        const uint16_t* vt = v_lds[buf];
+        // K operand of block h: token c, dims 32 k + 8 r .. +7
+        QV ka[2][KS];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = h * kBlock + c;
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+                ka[h][k] = *reinterpret_cast<const QV*>(kt + row * D + ((4 * k + r) ^ chunk_swizzle<D>(row)) * 8);
+        }
+        const int tok = 2 * j * kBlock + 4 * r;
+        QV pb[R];
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) {
+            f32x4_t S0 = {0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                S0 = mma_k32<QDT>(ka[0][k], qb[rg][k], S0);
+                S1 = mma_k32<QDT>(ka[1][k], qb[rg][k], S1);
+            }
+            float z[8] = {S0[0], S0[1], S0[2], S0[3], S1[0], S1[1], S1[2], S1[3]};
+            if (masked) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int t = tok + (i >> 2) * kBlock + (i & 3);
+                    z[i] = (t < n && t <= see[rg]) ? z[i] : -INFINITY;   // select, never 0 * garbage
+                }
+            }
+            const float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                                   fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+            const float m_blk = across_rows_max(mx) * qscale;
+            if (__builtin_amdgcn_ballot_w64(m_blk > m_run[rg] + kLazy) != 0) {
+                const float m_new = m_blk > m_run[rg] + kLazy ? m_blk : m_run[rg];
+                const float alpha = m_new == m_run[rg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
+                l_run[rg] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[rg][mt] *= alpha;
+                m_run[rg] = m_new;
+            }
+            const float neg_m = m_run[rg] == -INFINITY ? 0.0f : -m_run[rg];
+            float pr[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(z[i], qscale, neg_m));
+            // l sums the rounded weights P.V multiplies (a normalised average of them)
+            const uint4 pw = make_uint4(pack2<QDT>(pr[0], pr[1]), pack2<QDT>(pr[2], pr[3]),
+                                        pack2<QDT>(pr[4], pr[5]), pack2<QDT>(pr[6], pr[7]));
+            l_run[rg] += across_rows_sum((sum2<QDT>(pw.x) + sum2<QDT>(pw.y)) + (sum2<QDT>(pw.z) + sum2<QDT>(pw.w)));
+            pb[rg] = __builtin_bit_cast(QV, pw);
+        }
+        // V^T operand, dims 16 mt + c, tokens 4 r .. +3 of block 0 then of block 1.
+        // ds_read_b64_tr_b16 builds, in each 16-lane group, row k from the 4
+        // elements lanes 4k .. 4k + 3 point at and hands lane i element i of rows
+        // 0 .. 3; so lane (r, c) points at token 4 r + c / 4, dims 16 mt + 4 (c % 4).
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            uint2 vh[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = h * kBlock + 4 * r + (c >> 2);
+                const int lc = 2 * mt + ((c & 3) >> 1);
+                const uint16_t* src = vt + row * D + (lc ^ chunk_swizzle<D>(row)) * 8 + (c & 1) * 4;
+                vh[h] = __builtin_bit_cast(
+                    uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)src));
+            }
+            const QV va = __builtin_bit_cast(QV, make_uint4(vh[0].x, vh[0].y, vh[1].x, vh[1].y));
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg) acc[rg][mt] = mma_k32<QDT>(va, pb[rg], acc[rg][mt]);
+        }
+    };
+
+#pragma unroll
+    for (int jj = 0; jj < kStages - 1; ++jj)
+        if (jj < n_it) issue(jj);
+    for (int j = 0; j < n_it; ++j) {
+        // stage j has landed once only the later stages' loads are outstanding;
+        // the barrier also means every wave is done with stage j - 1's buffer
+        if (j + kStages - 2 < n_it) wait_loads_then_barrier<LPS * (kStages - 2)>();
+        else wait_loads_then_barrier<0>();
+        if (j + kStages - 1 < n_it) issue(j + kStages - 1);
+        const int t0 = 2 * j * kBlock;
+        compute(!(t0 + 2 * kBlock <= n && t0 + 2 * kBlock - 1 <= wg_min_see), j, j % kStages);
+    }
+
+    uint16_t* o16 = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) {
+        if (!live[rg]) continue;
+        const int row = rg * 16 + c;
+        const float inv = l_run[rg] > 0.0f ? 1.0f / l_run[rg] : 0.0f;
+        const int64_t orow = ((int64_t)(q0 + i_row[rg]) * p.H_q + hq0 + row % gs) * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            uint16_t e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] = to_q16<QDT>(acc[rg][mt][i] * inv);
+            *reinterpret_cast<uint2*>(o16 + orow + 16 * mt + 4 * r) =
+                make_uint2((uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16));
+        }
+    }
+}
+
 using KernelFn = void (*)(PrefillParams);
 
 template <int KDT, int QDT>
@@ -410,9 +671,18 @@ KernelFn pick_d(int D) {
     }
 }
 
+template <int KDT>
+KernelFn pick_dma(int D) {
+    switch (D) {
+        case 64: return paged_prefill_dma_kernel<KDT, 64>;
+        case 128: return paged_prefill_dma_kernel<KDT, 128>;
+        default: return nullptr;
+    }
+}
+
 KernelFn pick(int kdt, int qdt, int D) {
-    if (kdt == DT_F16 && qdt == DT_F16) return pick_d<DT_F16, DT_F16>(D);
-    if (kdt == DT_BF16 && qdt == DT_BF16) return pick_d<DT_BF16, DT_BF16>(D);
+    if (kdt == DT_F16 && qdt == DT_F16) return pick_dma<DT_F16>(D);
+    if (kdt == DT_BF16 && qdt == DT_BF16) return pick_dma<DT_BF16>(D);
     if (kdt == DT_FP8 && qdt == DT_BF16) return pick_d<DT_FP8, DT_BF16>(D);
     if (kdt == DT_FP8 && qdt == DT_F16) return pick_d<DT_FP8, DT_F16>(D);
     return nullptr;
