@@ -431,6 +431,69 @@ __device__ __forceinline__ void wait_loads_then_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Plain maxima of finite-or-minus-infinity values.  Written in asm because
+// fmaxf must quiet signalling NaNs and costs an extra v_max per operand here.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Max across the four lanes of a row (l % 16 equal): v_permlane16_swap pairs
+// row r with row r ^ 1 (lanes 16 apart), v_permlane32_swap pairs r with r ^ 2.
+__device__ __forceinline__ float row_max4(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float m = vmax3(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]), v);
+    const uint32_t w = __builtin_bit_cast(uint32_t, m);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return vmax3(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]), m);
+}
+
+__device__ __forceinline__ float row_sum4(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float s = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+    const uint32_t w = __builtin_bit_cast(uint32_t, s);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
+}
+
+// acc + the two 16-bit values of type T packed in w (v_dot2 against (1, 1):
+// the products are exact, the sum rounds once as a plain fp32 add would).
+template <int T>
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    if constexpr (T == DT_BF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, 0x3f803f80u),
+                                               acc, false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc,
+                                      false);
+}
+
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+
+// Eight ds_read_b64_tr_b16: at a[m] and at a[m] + OFF bytes (the same rows of
+// the next block), then a wait for them.  In asm because the compiler, unable
+// to tell these reads from the stage loads still landing in other LDS buffers,
+// would otherwise drain every outstanding vector-memory load first.
+template <int OFF>
+__device__ __forceinline__ void tr_read8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x2_t (&o)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(OFF)
+        : "memory");
+}
+
 // A wave-uniform 32-bit read through the scalar cache.  The compiler would
 // issue it as a vector load inside the stage loop (it cannot prove the table
 // unclobbered by the LDS-bound loads) and then drain the vector counter.
@@ -526,21 +589,30 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         ld_row[i] = row;
         ld_off[i] = (row % kBlock) * ROWB + ((pch ^ chunk_swizzle<D>(row)) * 16);
     }
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto issue = [&](int jj) {                 // the loads of stage jj (blocks 2 jj, 2 jj + 1)
         // wave-uniform table reads: scalar loads, which do not count against the
         // vector-memory counter the stage waits use
         const int ph0 = scalar_read(table + 2 * jj);
         const int ph1 = 2 * jj + 1 < nblk ? scalar_read(table + 2 * jj + 1) : -1;
+        const bool ok0 = ph0 >= 0 && ph0 < p.num_blocks, ok1 = ph1 >= 0 && ph1 < p.num_blocks;
+        const bool full = ok0 && ok1 && (2 * jj + 2) * kBlock <= n;          // uniform
         const int buf = jj % kStages;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int row = ld_row[i];
-            const int ph = row >= kBlock ? ph1 : ph0;
-            const bool ok = ph >= 0 && ph < p.num_blocks && 2 * jj * kBlock + row < n;
-            const int64_t off = (int64_t)ph * blk_stride + ld_off[i];
-            const char* ks = ok ? kbase + off : zero + ld_off[i];
-            const char* vs = ok ? vbase + off : zero + ld_off[i];
-            const int dst = (wave * NI + i) * 64 * 8;          // 16-bit elements
+            const int h = ((wave_u * NI + i) * (64 / CH)) / kBlock;          // uniform: block of this load
+            const int ph = h ? ph1 : ph0;
+            const int dst = (wave_u * NI + i) * 64 * 8;                       // 16-bit elements
+            const char* ks;
+            const char* vs;
+            if (full) {                        // uniform base + 32-bit lane offset
+                ks = kbase + (int64_t)ph * blk_stride + (uint32_t)ld_off[i];
+                vs = vbase + (int64_t)ph * blk_stride + (uint32_t)ld_off[i];
+            } else {
+                const bool ok = (h ? ok1 : ok0) && 2 * jj * kBlock + ld_row[i] < n;
+                ks = ok ? kbase + (int64_t)ph * blk_stride + ld_off[i] : zero + ld_off[i];
+                vs = ok ? vbase + (int64_t)ph * blk_stride + ld_off[i] : zero + ld_off[i];
+            }
             __builtin_amdgcn_global_load_lds(ks, (lds_void*)&k_lds[buf][dst], 16, 0, 0);
             __builtin_amdgcn_global_load_lds(vs, (lds_void*)&v_lds[buf][dst], 16, 0, 0);
         }
@@ -581,15 +653,14 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
             }
             float z[8] = {S0[0], S0[1], S0[2], S0[3], S1[0], S1[1], S1[2], S1[3]};
             if (masked) {
+                // token tok + (i / 4) * 16 + i % 4 is visible iff that offset <= lim
+                const int lim = min(n - 1, see[rg]) - tok;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int t = tok + (i >> 2) * kBlock + (i & 3);
-                    z[i] = (t < n && t <= see[rg]) ? z[i] : -INFINITY;   // select, never 0 * garbage
-                }
+                for (int i = 0; i < 8; ++i)
+                    z[i] = (i >> 2) * kBlock + (i & 3) <= lim ? z[i] : -INFINITY;   // select, never 0 * garbage
             }
-            const float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                                   fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-            const float m_blk = across_rows_max(mx) * qscale;
+            const float mx = vmax3(vmax3(z[0], z[1], z[2]), vmax3(z[3], z[4], z[5]), vmax3(z[6], z[7], z[7]));
+            const float m_blk = row_max4(mx) * qscale;
             if (__builtin_amdgcn_ballot_w64(m_blk > m_run[rg] + kLazy) != 0) {
                 const float m_new = m_blk > m_run[rg] + kLazy ? m_blk : m_run[rg];
                 const float alpha = m_new == m_run[rg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
@@ -602,30 +673,38 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
             float pr[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(z[i], qscale, neg_m));
-            // l sums the rounded weights P.V multiplies (a normalised average of them)
+            // l sums the rounded weights P.V multiplies (a normalised average of
+            // them); each lane keeps the part of its own tokens, all four lanes of
+            // a row rescale alike, and the parts are added at the end
             const uint4 pw = make_uint4(pack2<QDT>(pr[0], pr[1]), pack2<QDT>(pr[2], pr[3]),
                                         pack2<QDT>(pr[4], pr[5]), pack2<QDT>(pr[6], pr[7]));
-            l_run[rg] += across_rows_sum((sum2<QDT>(pw.x) + sum2<QDT>(pw.y)) + (sum2<QDT>(pw.z) + sum2<QDT>(pw.w)));
+            l_run[rg] = add_pair<QDT>(pw.w, add_pair<QDT>(pw.z, add_pair<QDT>(pw.y, add_pair<QDT>(pw.x, l_run[rg]))));
             pb[rg] = __builtin_bit_cast(QV, pw);
         }
         // V^T operand, dims 16 mt + c, tokens 4 r .. +3 of block 0 then of block 1.
         // ds_read_b64_tr_b16 builds, in each 16-lane group, row k from the 4
         // elements lanes 4k .. 4k + 3 point at and hands lane i element i of rows
         // 0 .. 3; so lane (r, c) points at token 4 r + c / 4, dims 16 mt + 4 (c % 4).
+        // Block 1's rows sit 16 rows (16 * ROWB bytes) after block 0's, with the same swizzle.
+        const int vrow = 4 * r + (c >> 2);
+        const uint32_t vrow_addr =
+            (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)(vt + vrow * D) + (c & 1) * 8;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            uint2 vh[2];
+        for (int m4 = 0; m4 < MT; m4 += 4) {
+            uint32_t a[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int row = h * kBlock + 4 * r + (c >> 2);
-                const int lc = 2 * mt + ((c & 3) >> 1);
-                const uint16_t* src = vt + row * D + (lc ^ chunk_swizzle<D>(row)) * 8 + (c & 1) * 4;
-                vh[h] = __builtin_bit_cast(
-                    uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)src));
+            for (int u = 0; u < 4; ++u) {
+                const int lc = 2 * (m4 + u) + ((c & 3) >> 1);
+                a[u] = vrow_addr + (uint32_t)((lc ^ chunk_swizzle<D>(vrow)) * 16);
             }
-            const QV va = __builtin_bit_cast(QV, make_uint4(vh[0].x, vh[0].y, vh[1].x, vh[1].y));
+            u32x2_t vh[8];
+            tr_read8<kBlock * ROWB>(a[0], a[1], a[2], a[3], vh);
 #pragma unroll
-            for (int rg = 0; rg < R; ++rg) acc[rg][mt] = mma_k32<QDT>(va, pb[rg], acc[rg][mt]);
+            for (int u = 0; u < 4; ++u) {
+                const QV va = __builtin_bit_cast(QV, make_uint4(vh[2 * u].x, vh[2 * u].y, vh[2 * u + 1].x, vh[2 * u + 1].y));
+#pragma unroll
+                for (int rg = 0; rg < R; ++rg) acc[rg][m4 + u] = mma_k32<QDT>(va, pb[rg], acc[rg][m4 + u]);
+            }
         }
     };
 
@@ -643,6 +722,8 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     }
 
     uint16_t* o16 = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) l_run[rg] = row_sum4(l_run[rg]);
 #pragma unroll
     for (int rg = 0; rg < R; ++rg) {
         if (!live[rg]) continue;

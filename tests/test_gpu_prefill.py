@@ -211,3 +211,14 @@ def test_prefill_long_context_sampled():
                                         c.scale)
         check(got[t:t + 1], want, wl.BF16, wl.BF16, f"row {t}")
     c.close()
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+@pytest.mark.parametrize("kv_dt", [wl.BF16, wl.E4M3])
+def test_prefill_scale_sign(scale, kv_dt):
+    """A negative softmax scale (the logits' order reverses) and a zero scale
+    (uniform weights over the visible positions) against the oracle."""
+    c = Case(kv_dt, 16, 4, 128, [(300, 45), (40, 40)], seed=12)
+    c.scale = float(np.float32(scale))
+    check(c.run(), c.expected(), kv_dt, c.q_dt, f"scale={scale}")
+    c.close()
