@@ -12,6 +12,8 @@ Contents
     row attends to all earlier rows), the "recompute everything" path that the
     cached decode must reproduce.
   * ``allocator_model``: a pure-Python model of the block pool allocator.
+  * ``int8_minmax``: the INT8 per-block min-max codes, their values, and a
+    model of the tiles as appends leave them.
 
 Pins (checked by the CPU tests, never by the oracle against itself):
   kv_cache_bytes   -- numbers the pages print (tests/golden/kv_sizes.json)
@@ -19,6 +21,10 @@ Pins (checked by the CPU tests, never by the oracle against itself):
   E4M3 decode      -- torch.float8_e4m3fn on all 256 codes; spec constants
   E4M3 encode      -- torch's RNE cast inside the finite range; saturation
                       and NaN from the specification
+  INT8 min-max     -- the page's formula on closed-form inputs, the half-step
+                      round-trip bound, range = min/max of the raw inputs since
+                      row 0, untouched rows when the range holds, and the
+                      re-encode error bound over whole fill sequences
   decode attention -- numpy textbook softmax, closed forms (single token,
                       two tokens, q = 0, constant V), GQA == repeated-KV MHA,
                       cached decode == causal recompute
@@ -31,12 +37,14 @@ import os
 import numpy as np
 
 from . import allocator_model  # noqa: F401  (re-exported)
+from . import int8_minmax  # noqa: F401  (re-exported)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 F32, F16, BF16, E4M3 = 0, 1, 2, 3
-_NP_STORAGE = {F32: np.float32, F16: np.float16, BF16: np.uint16, E4M3: np.uint8}
+F64 = 5     # K/V given as fp64 values (INT8 pools: the values their codes stand for)
+_NP_STORAGE = {F32: np.float32, F16: np.float16, BF16: np.uint16, E4M3: np.uint8, F64: np.float64}
 
 _lib = None
 

@@ -28,7 +28,8 @@
 
 /* Storage type codes of this oracle (numerically equal to the library's by
  * convention, so the harness can pass one integer; defined independently). */
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_E4M3 = 3 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_E4M3 = 3, OR_F64 = 5 };   /* OR_F64: values already
+                                                                           dequantised by the caller */
 
 /* ------------------------------------------------------------------------
  * KV size formula.  [cf1] §1.2: per token, 2 (K and V) x layers x KV heads x
@@ -128,6 +129,7 @@ void oracle_widen_array(const void* src, int32_t dtype, int64_t n, double* out) 
             case OR_F16: out[i] = oracle_f16_to_f64(((const uint16_t*)src)[i]); break;
             case OR_BF16: out[i] = oracle_bf16_to_f64(((const uint16_t*)src)[i]); break;
             case OR_E4M3: out[i] = oracle_e4m3_to_f64(((const uint8_t*)src)[i]); break;
+            case OR_F64: out[i] = ((const double*)src)[i]; break;
             default: out[i] = NAN;
         }
     }
@@ -139,6 +141,7 @@ static double widen(const void* base, int32_t dtype, int64_t i) {
         case OR_F16: return oracle_f16_to_f64(((const uint16_t*)base)[i]);
         case OR_BF16: return oracle_bf16_to_f64(((const uint16_t*)base)[i]);
         case OR_E4M3: return oracle_e4m3_to_f64(((const uint8_t*)base)[i]);
+        case OR_F64: return ((const double*)base)[i];
         default: return NAN;
     }
 }

@@ -53,6 +53,50 @@ MUTANTS = {
 }
 
 
+MUTANTS["f64_storage_narrowed"] = ("case OR_F64: return ((const double*)base)[i];",
+                                   "case OR_F64: return (float)((const double*)base)[i];",
+                                   [pins.check_f64_storage_path])
+
+# The INT8 model is Python: its mutants are loaded as a fresh module.
+I8_SRC = os.path.join(os.path.dirname(oracle.__file__), "int8_minmax.py")
+I8_MUTANTS = {
+    "int8_scale_256": ("np.rint(t * F32(255))", "np.rint(t * F32(256))", [pins.check_int8_formula]),
+    "int8_truncates": ("np.rint(t * F32(255))", "np.floor(t * F32(255))", [pins.check_int8_formula]),
+    "int8_ties_down": ("np.rint(t * F32(255))", "np.ceil(t * F32(255) - F32(0.5))", [pins.check_int8_formula]),
+    "int8_offset_from_max": ("d = x - lo", "d = hi - x", [pins.check_int8_formula, pins.check_int8_round_trip]),
+    "int8_value_over_256": ("(lo * (255.0 - c) + hi * c) / 255.0", "(lo * (256.0 - c) + hi * c) / 256.0",
+                            [pins.check_int8_round_trip]),
+    "int8_value_reversed": ("(lo * (255.0 - c) + hi * c) / 255.0", "(hi * (255.0 - c) + lo * c) / 255.0",
+                            [pins.check_int8_round_trip]),
+    "int8_no_restart_at_row0": ("if 0 not in new:", "if True:", [pins.check_int8_fill_invariants]),
+    "int8_range_not_widened": ("lo, hi = min(old_lo, lo), max(old_hi, hi)", "lo, hi = lo, hi",
+                               [pins.check_int8_fill_invariants]),
+    "int8_no_reencode": ("codes[rest] = encode(value_f32(codes[rest], old_lo, old_hi), lo, hi)", "pass",
+                         [pins.check_int8_fill_invariants]),
+    "int8_reencode_reads_new_range": ("value_f32(codes[rest], old_lo, old_hi)", "value_f32(codes[rest], lo, hi)",
+                                      [pins.check_int8_fill_invariants]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(I8_MUTANTS))
+def test_planted_int8_mistake_is_caught(name):
+    import importlib.util
+    find, repl, checks = I8_MUTANTS[name]
+    with open(I8_SRC) as f:
+        src = f.read()
+    assert find in src, f"mutation site vanished: {find!r}"
+    spec = importlib.util.spec_from_loader(f"int8_mutant_{name}", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(src.replace(find, repl), f"<{name}>", "exec"), mod.__dict__)
+    caught = []
+    for check in checks:
+        try:
+            check(mod)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"planted mistake {name!r} passed every pin"
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name, tmp_path, monkeypatch):
     find, repl, checks = MUTANTS[name]

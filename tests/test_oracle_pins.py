@@ -439,3 +439,126 @@ ALL_CHECKS = [check_kv_sizes, check_f16_widen, check_bf16_widen, check_e4m3_deco
               check_fp8_attention_on_dequantised_values, check_prefill_vs_library_attention,
               check_prefill_single_token_is_decode, check_prefill_chunks_compose,
               check_prefill_fp8_on_dequantised_values]
+
+
+# ---------------------------------------------------------------------------
+# INT8 per-block min-max codes ([moo] §3.3): q = round((k - k_min) / (k_max - k_min) * 255)
+# ---------------------------------------------------------------------------
+from fractions import Fraction  # noqa: E402
+
+from oracle import int8_minmax as _i8  # noqa: E402
+
+
+def _half_even(fr: Fraction) -> int:
+    lo = fr.numerator // fr.denominator
+    rem = fr - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        return lo + 1
+    return lo
+
+
+def check_int8_formula(m=_i8):
+    """Inputs for which every fp32 step of the formula is exact, against the
+    formula evaluated in rationals with round-half-even."""
+    cases = [(0.0, 256.0, [float(k) for k in range(257)]),          # t = k/256, codes 255k/256
+             (-3.0, 5.0, [-3.0 + j for j in range(9)]),             # t = j/8
+             (-1.0, 1.0, [-1.0, -0.5, 0.0, 0.5, 1.0])]              # 0 -> 127.5 -> 128 (even)
+    for lo, hi, xs in cases:
+        got = m.encode(np.array(xs, np.float32), lo, hi)
+        want = [_half_even((Fraction(x) - Fraction(lo)) / (Fraction(hi) - Fraction(lo)) * 255) for x in xs]
+        assert got.tolist() == want, (lo, hi)
+    assert m.encode(np.float32(0.0), -1.0, 1.0) == 128
+    # degenerate range: code 0, standing for the value itself
+    assert m.encode(np.float32(2.5), 2.5, 2.5) == 0 and m.value(np.uint8(0), 2.5, 2.5) == 2.5
+
+
+def check_int8_round_trip(m=_i8):
+    """A code stands for its input within half a step; the range's ends are exact."""
+    rng = np.random.default_rng(41)
+    for lo, hi in [(-2.5, 3.75), (0.001, 0.002), (-100.0, -99.0), (-1e-3, 7e3)]:
+        lo, hi = np.float32(lo), np.float32(hi)
+        x = rng.uniform(lo, hi, 4000).astype(np.float32)
+        x[:2] = (lo, hi)
+        c = m.encode(x, lo, hi)
+        assert c[0] == 0 and c[1] == 255
+        half = (float(hi) - float(lo)) / 510.0
+        assert np.all(np.abs(m.value(c, lo, hi) - x) <= half * (1 + 1e-4)), (lo, hi)
+        assert m.value(np.uint8(0), lo, hi) == float(lo) and m.value(np.uint8(255), lo, hi) == float(hi)
+
+
+def check_int8_fill_invariants(m=_i8):
+    """Tiles filled a random number of rows per call: the range is the min and
+    max of the raw values since row 0, rows keep their codes while the range
+    holds, every row stays within its accumulated re-encode bound of its raw
+    value, and writing row 0 again starts the tile over."""
+    rng = np.random.default_rng(43)
+    H, D = 2, 16
+    for trial in range(25):
+        store = m.TileStore(H, D)
+        for b in (3, 7):
+            raw = {"k": [], "v": []}
+            bound = {"k": np.zeros((16, H)), "v": np.zeros((16, H))}
+            row = 0
+            while row < 16:
+                n = int(min(rng.integers(1, 6), 16 - row))
+                scale = float(rng.choice([0.25, 1.0, 4.0]))
+                K = (rng.standard_normal((n, H, D)) * scale).astype(np.float32)
+                V = (rng.standard_normal((n, H, D)) * scale).astype(np.float32)
+                before = {(kind, g): store.tile(kind, b, g) for kind in "kv" for g in range(H)}
+                store.append(np.arange(n) + 16 * b + row, K, V)
+                for kind, X in (("k", K), ("v", V)):
+                    raw[kind].extend(X)
+                    R = np.stack(raw[kind])                                    # [rows][H][D]
+                    for g in range(H):
+                        codes, (lo, hi) = store.tile(kind, b, g)
+                        assert lo == R[:, g].min() and hi == R[:, g].max(), (trial, kind, row)
+                        old_codes, (olo, ohi) = before[(kind, g)]
+                        if row > 0 and (olo, ohi) == (lo, hi):
+                            assert np.array_equal(codes[:row], old_codes[:row])
+                        half = (float(hi) - float(lo)) / 510.0 * (1 + 1e-4) + 1e-6 * max(abs(float(lo)), abs(float(hi)))
+                        if row > 0 and (olo, ohi) != (lo, hi):
+                            bound[kind][:row, g] += half                       # one more re-encode
+                        bound[kind][row:row + n, g] = half
+                        err = np.abs(m.value(codes[:row + n], lo, hi) - R[:, g]).max(axis=1)
+                        assert np.all(err <= bound[kind][:row + n, g]), (trial, kind, row)
+                row += n
+        # row 0 again: the tile starts over with this call's values alone
+        K = rng.standard_normal((1, H, D)).astype(np.float32) * 0.01
+        store.append(np.array([16 * 3]), K, K)
+        for g in range(H):
+            _, (lo, hi) = store.tile("k", 3, g)
+            assert lo == K[0, g].min() and hi == K[0, g].max()
+
+
+def check_f64_storage_path():
+    """Attention on fp64 storage: equal to fp32 storage of the same values, and
+    to the textbook softmax on values that fp32 cannot hold."""
+    rng = np.random.default_rng(44)
+    q = rng.standard_normal((2, 4, 16)).astype(np.float32)
+    K = rng.standard_normal((50, 2, 16)).astype(np.float32)
+    V = rng.standard_normal((50, 2, 16)).astype(np.float32)
+    off, lens = np.array([0, 20]), np.array([20, 30], np.int32)
+    a = oracle.decode_attention(q, oracle.F32, K, V, oracle.F32, off, lens, 0.25)
+    b = oracle.decode_attention(q, oracle.F32, K.astype(np.float64), V.astype(np.float64), oracle.F64, off, lens, 0.25)
+    assert np.array_equal(a, b)
+    K64 = rng.standard_normal((50, 2, 16)) * (1 + 1e-9)
+    V64 = rng.standard_normal((50, 2, 16)) * (1 + 1e-9)
+    got = oracle.decode_attention(q, oracle.F32, K64, V64, oracle.F64, off, lens, 0.25)
+    ref = _textbook(q.astype(np.float64), K64, V64, off, lens, 0.25)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_int8_formula_closed_forms():
+    check_int8_formula()
+
+
+def test_int8_round_trip_half_step():
+    check_int8_round_trip()
+
+
+def test_int8_fill_invariants():
+    check_int8_fill_invariants()
+
+
+def test_f64_storage_path():
+    check_f64_storage_path()
