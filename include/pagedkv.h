@@ -55,19 +55,25 @@ typedef enum {
     PKV_F32 = 0,
     PKV_F16 = 1,
     PKV_BF16 = 2,
-    PKV_FP8_E4M3 = 3           /* OCP 8-bit float E4M3 ("FN": max 448, NaN 0x7F/0xFF) */
+    PKV_FP8_E4M3 = 3,          /* OCP 8-bit float E4M3 ("FN": max 448, NaN 0x7F/0xFF) */
+    PKV_INT8_MINMAX = 4        /* 8-bit codes with a min-max range per (block, KV head) tile,
+                                  [moo] §3.3; see kv_append */
 } pkv_dtype;
 
 typedef struct kv_pool kv_pool_t;
 
 typedef struct {
-    void* k_pool;              /* device; [num_blocks][kv_heads][block_size][head_dim] */
+    void* k_pool;              /* device; [num_blocks][kv_heads] tiles of block_bytes: the tile is
+                                  [block_size][head_dim] elements (INT8: codes, then a 16-byte
+                                  header {min, max, step, 0} as fp32) */
     void* v_pool;              /* device; same layout, separate buffer */
     float* k_scale;            /* device; [kv_heads] (FP8 pools only, else NULL) */
     float* v_scale;            /* device; [kv_heads] (FP8 pools only, else NULL) */
     uint64_t pool_bytes;       /* bytes of ONE of k_pool / v_pool */
-    uint64_t block_bytes;      /* bytes of one (block, kv head) tile = block_size*head_dim*elem */
-    uint64_t total_bytes;      /* device bytes owned: 2*pool_bytes + scales + a 4 KiB zero tile */
+    uint64_t block_bytes;      /* bytes of one (block, kv head) tile = block_size*head_dim*elem
+                                  (+ 16 for the INT8 header) */
+    uint64_t total_bytes;      /* device bytes owned: 2*pool_bytes + scales + a 4 KiB zero tile
+                                  (+ 8 bytes per slot of append tags for INT8 pools) */
     int32_t num_blocks, block_size, kv_heads, head_dim, dtype, elem_bytes;
     int32_t free_blocks;       /* refcount 0 */
     int32_t used_blocks;       /* refcount >= 1 */
@@ -266,9 +272,26 @@ int kv_free_list(const kv_pool_t* pool, int32_t* out, int32_t cap, int32_t* n);
  *   k_new, v_new  device, [T][kv_heads][head_dim] of src_dtype, 16-byte
  *                 aligned.  src_dtype must equal the pool dtype, or be BF16
  *                 or F32 for an FP8 pool, which quantises in the kernel:
- *                 code = E4M3_rne_satfinite(x * inv_scale[g]), NaN -> 0x7F.
- * T == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED (dtype pairing),
- * STATE (host-only pool), DEVICE (launch). */
+ *                 code = E4M3_rne_satfinite(x * inv_scale[g]), NaN -> 0x7F;
+ *                 or BF16, F16 or F32 for an INT8 pool (below).
+ * T == 0 is a no-op.
+ *
+ * INT8 pools ([moo] §3.3, per-block min-max): src_dtype is BF16, F16 or F32.
+ * Each (block, KV head) tile keeps, for K and for V separately, a range
+ * (min, max) and codes q = round_half_even((x - min) / (max - min) * 255),
+ * every step in fp32 (max == min gives 0); a code stands for
+ * min + q * (max - min) / 255.  The range is the min and max of every value
+ * written into the tile since its row 0 was last written: a call that writes
+ * row 0 of a tile starts it afresh (its other rows no longer count); any
+ * other call widens the range to take its values and, if the range moved,
+ * re-encodes the tile's other rows from their fp32 values min + q * step
+ * (step = (max - min) / 255).  All rows one call writes into a tile are taken
+ * together.  Inputs must be finite.  Two kernels run: one tags each written
+ * slot with the call, one encodes each touched tile; the tags are the
+ * library's, so calls on one pool must not overlap on the device.
+ *
+ * Errors: INVALID_ARG, UNSUPPORTED (dtype pairing), STATE (host-only pool),
+ * DEVICE (launch). */
 int kv_append(kv_pool_t* pool, const int32_t* slot_mapping, int32_t T,
               const void* k_new, const void* v_new, int32_t src_dtype, void* stream);
 
@@ -280,9 +303,10 @@ int kv_append(kv_pool_t* pool, const int32_t* slot_mapping, int32_t T,
  *         newest token, appended before the call, is j = n-1)
  *   out[b][h] = sum_j softmax(z)_j * V_b[j][g]
  * where K_b[j] lives in block block_tables[b][j / 16], row j % 16.  For an FP8
- * pool the stored values are decode(code) * k_scale[g] (resp. v_scale[g]).
+ * pool the stored values are decode(code) * k_scale[g] (resp. v_scale[g]); for
+ * an INT8 pool, min + code * (max - min) / 255 of the token's tile.
  *   q             device [B][H_q][head_dim] of q_dtype (= pool dtype; BF16
- *                 for an FP8 pool), 16-byte aligned.
+ *                 or F16 for an FP8 or INT8 pool), 16-byte aligned.
  *   block_tables  device [B][max_blocks_per_seq] int32.  Entries outside
  *                 [0, num_blocks) make their 16 tokens count as absent.
  *   context_lens  device [B] int32, each clamped to
@@ -375,7 +399,7 @@ int kv_seq_swap_in(kv_pool_t* pool, int32_t seq, const void* host_src, size_t by
  * size.  Q.K^T and P.V run on the matrix cores.  Asynchronous on stream; no
  * workspace.  Device contents are not validated (q_start out of order or
  * q_len_s > n_s is undefined).  Errors: INVALID_ARG, UNSUPPORTED (F32 pool,
- * other head_dim), STATE (host-only pool), DEVICE. */
+ * other head_dim, INT8 pool), STATE (host-only pool), DEVICE. */
 int paged_prefill(kv_pool_t* pool, const void* q, int32_t q_dtype, int32_t n_seqs, int32_t H_q,
                   const int32_t* q_start, int32_t total_q, int32_t max_q_len,
                   const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -19,7 +19,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
-F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+F32, F16, BF16, FP8_E4M3, INT8_MINMAX = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_NO_BLOCKS, ERR_OUT_OF_RANGE, ERR_STATE, ERR_UNSUPPORTED, ERR_DEVICE = range(7)
 BLOCK = 16
 
@@ -154,7 +154,7 @@ def torch_dtype(code: int):
     torch = _torch()
     if _TORCH_DTYPES is None:
         _TORCH_DTYPES = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16,
-                         FP8_E4M3: torch.uint8}
+                         FP8_E4M3: torch.uint8, INT8_MINMAX: torch.uint8}
     return _TORCH_DTYPES[code]
 
 

@@ -106,6 +106,114 @@ __global__ __launch_bounds__(256) void kv_append_fp8(AppendParams p) {
     *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
 }
 
+// ---------------------------------------------------------------------------
+// INT8 per-block min-max (www.mooersco.com/news/1484987 §3.3): codes
+// q = round((x - min) / (max - min) * 255) with one (min, max) per (block, KV
+// head) tile, separately for K and V.  Every step is fp32 in the formula's
+// order, rounded once each (no fused multiply-add), so the codes are exactly
+// determined by the values and the order of the calls.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t int8_code(float x, float lo, float hi) {
+#pragma clang fp contract(off)
+    if (!(hi > lo)) return 0u;
+    const float t = (x - lo) / (hi - lo);                        // correctly rounded fp32 division
+    const float c = __builtin_rintf(t * 255.0f);                  // round half to even
+    if (!(c >= 0.0f)) return 0u;                                  // negative or NaN
+    return c >= 255.0f ? 255u : (uint32_t)c;
+}
+
+__device__ __forceinline__ float int8_step(float lo, float hi) { return (hi - lo) / 255.0f; }
+
+template <int SRC>
+__device__ __forceinline__ float src_value(const void* p, int64_t i) {
+    if constexpr (SRC == DT_F32) return reinterpret_cast<const float*>(p)[i];
+    else if constexpr (SRC == DT_F16) return (float)reinterpret_cast<const _Float16*>(p)[i];
+    else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);
+}
+
+// Pass 1: each written slot records (this call's epoch, token).
+__global__ __launch_bounds__(256) void kv_append_int8_tag(AppendParams p) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= p.T) return;
+    const int32_t slot = p.slots[t];
+    if (slot < 0 || (int64_t)slot >= p.num_slots) return;
+    p.tags[slot] = ((uint64_t)p.epoch << 32) | (uint32_t)t;
+}
+
+// Pass 2: one wave per (token, KV head).  The wave of the lowest token of this
+// call in a tile encodes the whole tile (K, then V); the others exit.  Lane r
+// < 16 learns which token writes row r this call (or none).
+template <int SRC>
+__global__ __launch_bounds__(64) void kv_append_int8(AppendParams p) {
+#pragma clang fp contract(off)   // a re-encoded value is min + code * step, rounded twice
+    const int t = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+    const int32_t slot = p.slots[t];
+    if (slot < 0 || (int64_t)slot >= p.num_slots) return;
+    const int64_t blk = slot / kBlock;
+    int writer = -1;
+    if (lane < kBlock) {
+        const uint64_t tag = p.tags[blk * kBlock + lane];
+        if ((uint32_t)(tag >> 32) == p.epoch) writer = (int)(uint32_t)tag;
+    }
+    int lowest = writer < 0 ? 0x7FFFFFFF : writer;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lowest = min(lowest, __shfl_xor(lowest, o, 64));
+    if (lowest != t) return;                             // uniform: another wave owns the tile
+    const uint32_t written = (uint32_t)__builtin_amdgcn_ballot_w64(lane < kBlock && writer >= 0) & 0xFFFFu;
+    const bool fresh = written & 1u;                     // row 0 written: the tile starts over
+    const int D = p.D;
+    const int64_t tile = tile_bytes(DT_INT8, D);
+    for (int which = 0; which < 2; ++which) {
+        uint8_t* base = reinterpret_cast<uint8_t*>(which ? p.v_pool : p.k_pool) + (blk * p.H_kv + g) * tile;
+        float* header = reinterpret_cast<float*>(base + (int64_t)kBlock * D);
+        const void* src = which ? p.v_src : p.k_src;
+        // the range of this call's values in the tile
+        float lo = INFINITY, hi = -INFINITY;
+        for (int r = 0; r < kBlock; ++r) {
+            if (!((written >> r) & 1u)) continue;        // uniform
+            const int tr = __shfl(writer, r, 64);
+            const int64_t row0 = ((int64_t)tr * p.H_kv + g) * D;
+            for (int e = lane; e < D; e += 64) {
+                const float x = src_value<SRC>(src, row0 + e);
+                lo = fminf(lo, x);
+                hi = fmaxf(hi, x);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            lo = fminf(lo, __shfl_xor(lo, o, 64));
+            hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+        }
+        if (!fresh) {
+            const float old_lo = header[0], old_hi = header[1];
+            const float new_lo = fminf(old_lo, lo), new_hi = fmaxf(old_hi, hi);
+            if (new_lo != old_lo || new_hi != old_hi) {  // the range moved: re-encode the other rows
+                const float old_step = int8_step(old_lo, old_hi);
+                for (int i = lane; i < kBlock * D; i += 64) {
+                    const int r = i / D;
+                    if ((written >> r) & 1u) continue;
+                    const float v = old_lo + (float)base[i] * old_step;   // two roundings (contract off)
+                    base[i] = (uint8_t)int8_code(v, new_lo, new_hi);
+                }
+            }
+            lo = new_lo;
+            hi = new_hi;
+        }
+        for (int r = 0; r < kBlock; ++r) {
+            if (!((written >> r) & 1u)) continue;
+            const int tr = __shfl(writer, r, 64);
+            const int64_t row0 = ((int64_t)tr * p.H_kv + g) * D;
+            for (int e = lane; e < D; e += 64) base[r * D + e] = (uint8_t)int8_code(src_value<SRC>(src, row0 + e), lo, hi);
+        }
+        if (lane == 0) {
+            header[0] = lo;
+            header[1] = hi;
+            header[2] = int8_step(lo, hi);
+            header[3] = 0.0f;
+        }
+    }
+}
+
 // Plain copy, 16 bytes per load/store, four independent chunks per thread per step.
 __global__ __launch_bounds__(256) void pkv_copy_kernel(uint4* __restrict__ dst,
                                                        const uint4* __restrict__ src, int64_t n) {
@@ -175,6 +283,17 @@ hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream) {
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream) {
     if (p.T <= 0) return hipSuccess;
     AppendParams arg = p;
+    if (p.dst_dt == DT_INT8) {
+        if (!p.tags || p.epoch == 0) return hipErrorInvalidValue;
+        void* args[] = {&arg};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kv_append_int8_tag),
+                                       dim3((unsigned)((p.T + 255) / 256)), dim3(256), args, 0, stream);
+        if (e != hipSuccess) return e;
+        const void* fn = p.src_dt == DT_F32   ? reinterpret_cast<const void*>(kv_append_int8<DT_F32>)
+                         : p.src_dt == DT_F16 ? reinterpret_cast<const void*>(kv_append_int8<DT_F16>)
+                                              : reinterpret_cast<const void*>(kv_append_int8<DT_BF16>);
+        return hipLaunchKernel(fn, dim3((unsigned)p.T, (unsigned)p.H_kv), dim3(64), args, 0, stream);
+    }
     if (p.dst_dt == p.src_dt) {
         int row_bytes = p.D * elem_bytes(p.dst_dt);
         const int64_t threads = 2LL * p.T * p.H_kv * (row_bytes / 16);

@@ -41,12 +41,14 @@ template <> struct Elem<DT_F32> { static constexpr int bytes = 4; };
 template <> struct Elem<DT_F16> { static constexpr int bytes = 2; };
 template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
 template <> struct Elem<DT_FP8> { static constexpr int bytes = 1; };
+template <> struct Elem<DT_INT8> { static constexpr int bytes = 1; };
 
 // Geometry of one (block, KV head) tile [16][D] of storage type DT.
 template <int DT, int D> struct Tile {
     static constexpr int E = Elem<DT>::bytes;
     static constexpr int ROW = D * E;                                // bytes of one token row
-    static constexpr int BYTES = kBlock * ROW;                       // bytes of the tile
+    static constexpr int BYTES = kBlock * ROW;                       // bytes of the tile's elements
+    static constexpr int STRIDE = BYTES + (DT == DT_INT8 ? kInt8HeaderBytes : 0);   // tile to tile
     static constexpr int W = BYTES / 64 >= 16 ? 16 : BYTES / 64;     // bytes per lane per load
     static constexpr int EPL = W / E;                                // elements per lane per load
     static constexpr int LPR = ROW / W;                              // lanes per token row
@@ -91,6 +93,9 @@ __device__ __forceinline__ void widen(const typename Raw<W>::T& r, float* f) {
         } else if constexpr (DT == DT_BF16) {
             f[2 * i] = bf16lo(w);
             f[2 * i + 1] = bf16hi(w);
+        } else if constexpr (DT == DT_INT8) {  // min-max codes as integers 0..255 (exact)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) f[4 * i + k] = (float)((w >> (8 * k)) & 0xFFu);
         } else {  // OCP E4M3 -> fp32, two codes per instruction
             auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
             auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
@@ -443,6 +448,22 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
             qf[h][e] = load_q<QDT>(p.q, ((int64_t)b * p.H_q + hq0 + h) * D + c * EPL + e) * qscale;
+    // INT8 pools: a key is min + step * code, so <qf, key> = min * sum(qf) +
+    // step * <qf, codes>; sum(qf) over the head is taken once.  The values'
+    // min term is kept apart per stream (mv) and added when the streams merge.
+    constexpr bool I8 = KDT == DT_INT8;
+    float qsum[GS], mv[GS];
+#pragma unroll
+    for (int h = 0; h < GS; ++h) {
+        qsum[h] = 0.0f;
+        mv[h] = 0.0f;
+        if constexpr (I8) {
+            float s = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s += qf[h][e];
+            qsum[h] = row_sum<LPR>(s);
+        }
+    }
 
     float m[GS], l[GS], acc[GS][EPL];
 #pragma unroll
@@ -457,8 +478,8 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
     const char* kbase = reinterpret_cast<const char*>(p.k_pool);
     const char* vbase = reinterpret_cast<const char*>(p.v_pool);
     const int lane_off = r * NLOAD * TL::ROW + c * TL::W;
-    const int64_t head_off = (int64_t)g * TL::BYTES;
-    const int64_t blk_stride = (int64_t)p.H_kv * TL::BYTES;
+    const int64_t head_off = (int64_t)g * TL::STRIDE;
+    const int64_t blk_stride = (int64_t)p.H_kv * TL::STRIDE;
     const int blk0 = R.blk_first + wave;
     const int nmine = blk0 < R.blk_last ? (R.blk_last - blk0 + kDecodeWaves - 1) / kDecodeWaves : 0;
     WaveTable wt;
@@ -466,6 +487,7 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
 
     struct Buf {
         RawT k[NLOAD], v[NLOAD];
+        float4 kh, vh;                   // INT8: tile headers {min, max, step, 0}
         bool ok;
     };
     auto fetch = [&](int j, Buf& B) {
@@ -473,11 +495,16 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
         const int phys = wt.phys(j);
         B.ok = phys >= 0 && phys < p.num_blocks;
         if (!B.ok) return;
-        const int64_t off = (int64_t)phys * blk_stride + head_off + lane_off;
+        const int64_t tile = (int64_t)phys * blk_stride + head_off;
+        const int64_t off = tile + lane_off;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
             B.k[i] = *reinterpret_cast<const RawT*>(kbase + off + i * TL::ROW);
             B.v[i] = *reinterpret_cast<const RawT*>(vbase + off + i * TL::ROW);
+        }
+        if constexpr (I8) {
+            B.kh = *reinterpret_cast<const float4*>(kbase + tile + TL::BYTES);
+            B.vh = *reinterpret_cast<const float4*>(vbase + tile + TL::BYTES);
         }
     };
     auto update = [&](auto masked, int blk, const Buf& B) {
@@ -497,6 +524,7 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) d = fmaf(qf[h][e], kf[e], d);
                 d = row_sum<LPR>(d);
+                if constexpr (I8) d = fmaf(B.kh.z, d, B.kh.x * qsum[h]);
                 z[h][i] = valid ? d : -INFINITY;
             }
             if (MASKED && !valid) {
@@ -520,6 +548,11 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
                 psum += pv[i];
             }
             l[h] = fmaf(l[h], alpha, psum);
+            if constexpr (I8) {
+                mv[h] = fmaf(mv[h], alpha, B.vh.x * psum);
+#pragma unroll
+                for (int i = 0; i < NLOAD; ++i) pv[i] *= B.vh.z;
+            }
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 float a = acc[h][e] * alpha;
@@ -542,7 +575,7 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
 #pragma unroll
     for (int h = 0; h < GS; ++h) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s_o[s][h][c * EPL + e] = acc[h][e];
+        for (int e = 0; e < EPL; ++e) s_o[s][h][c * EPL + e] = acc[h][e] + mv[h];
         if (c == 0) {
             s_m[s][h] = m[h];
             s_l[s][h] = l[h];
@@ -626,6 +659,7 @@ __device__ __forceinline__ float row_bcast(float v, int src_lane_in_row) {
 }
 
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
@@ -653,11 +687,28 @@ __device__ __forceinline__ void fp8_token_pairs(const uint2& a, const uint2& b, 
     }
 }
 
+// 8 INT8 min-max codes (two words) -> 8 bf16 / f16 values (integers 0..255, exact).
+template <int QDT>
+__device__ __forceinline__ typename MfmaIn<QDT>::T u8x8_to_mfma(uint2 w) {
+    const uint32_t ws[2] = {w.x, w.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t word = ws[j >> 1];
+        const int sh = 16 * (j & 1);
+        const f32x2_t v = {(float)((word >> sh) & 0xFFu), (float)((word >> (sh + 8)) & 0xFFu)};
+        if constexpr (QDT == DT_BF16) o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+        else o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    }
+    return __builtin_bit_cast(typename MfmaIn<QDT>::T, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
 template <int KDT>
 struct GqaTile {
     static constexpr int E = Elem<KDT>::bytes;
     static constexpr int ROW = 128 * E;                  // bytes of a token row
     static constexpr int BYTES = kBlock * ROW;
+    static constexpr int STRIDE = BYTES + (KDT == DT_INT8 ? kInt8HeaderBytes : 0);
     static constexpr int KW = 8 * E;                      // bytes per lane per MFMA step (8 dims)
     using KRaw = typename Raw<KW>::T;                     // uint4 (16-bit) or uint2 (FP8)
     using VRaw = typename Raw<KW>::T;
@@ -702,6 +753,18 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
     }
     float qscale = p.scale * kLog2e;
     if constexpr (KDT == DT_FP8) qscale *= p.k_scale[g];
+    // INT8 pools: <q, key> = min * sum(q) + step * <q, codes> (sum over the head,
+    // taken once); the values' min term is kept apart per stream (mv_run).
+    constexpr bool I8 = KDT == DT_INT8;
+    float qsum = 0.0f, mv_run = 0.0f;
+    if constexpr (I8) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qsum += (float)qb[s][e];
+        qsum += __shfl_xor(qsum, 16, 64);
+        qsum += __shfl_xor(qsum, 32, 64);
+    }
 
     float m_run = -INFINITY, l_run = 0.0f;   // stream (row r, head c)
     float acc[GS][8];
@@ -713,8 +776,8 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
     const int32_t* table = p.tables + (int64_t)b * p.max_blocks;
     const char* kbase = reinterpret_cast<const char*>(p.k_pool);
     const char* vbase = reinterpret_cast<const char*>(p.v_pool);
-    const int64_t head_off = (int64_t)g * TL::BYTES;
-    const int64_t blk_stride = (int64_t)p.H_kv * TL::BYTES;
+    const int64_t head_off = (int64_t)g * TL::STRIDE;
+    const int64_t blk_stride = (int64_t)p.H_kv * TL::STRIDE;
     // K: token c, step s -> bytes KW * (4 s + r); V: token 4 r + i, bytes KW * c.
     const int k_off = c * TL::ROW + r * TL::KW;
     const int v_off = (4 * r) * TL::ROW + c * TL::KW;
@@ -726,6 +789,7 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
     struct Buf {
         KRaw k[KS];
         KRaw v[4];
+        float4 kh, vh;                   // INT8: tile headers {min, max, step, 0}
         bool ok;
     };
     auto fetch = [&](int j, Buf& B) {
@@ -738,6 +802,10 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
         for (int s = 0; s < KS; ++s) B.k[s] = *reinterpret_cast<const KRaw*>(kbase + off + k_off + s * 4 * TL::KW);
 #pragma unroll
         for (int i = 0; i < 4; ++i) B.v[i] = *reinterpret_cast<const KRaw*>(vbase + off + v_off + i * TL::ROW);
+        if constexpr (I8) {
+            B.kh = *reinterpret_cast<const float4*>(kbase + off + TL::BYTES);
+            B.vh = *reinterpret_cast<const float4*>(vbase + off + TL::BYTES);
+        }
     };
     auto update = [&](auto masked, int blk, const Buf& B) {
         constexpr bool MASKED = decltype(masked)::value;
@@ -746,6 +814,7 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
         for (int s = 0; s < KS; ++s) {
             MT a;
             if constexpr (KDT == DT_FP8) a = fp8x8_to_mfma<QDT>(B.k[s]);
+            else if constexpr (I8) a = u8x8_to_mfma<QDT>(B.k[s]);
             else a = __builtin_bit_cast(MT, B.k[s]);
             S = mfma16x16x32<QDT>(a, qb[s], S);
         }
@@ -753,7 +822,8 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
         float z[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = S[i] * qscale;
+            if constexpr (I8) z[i] = fmaf(B.kh.z, S[i], B.kh.x * qsum) * qscale;
+            else z[i] = S[i] * qscale;
             if (MASKED && tok + i >= R.pend) z[i] = -INFINITY;
         }
         const float m_new = fmaxf(fmaxf(m_run, fmaxf(z[0], z[1])), fmaxf(z[2], z[3]));
@@ -763,6 +833,7 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
 #pragma unroll
         for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(z[i] - m_use);
         l_run = fmaf(l_run, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
+        if constexpr (I8) mv_run = fmaf(mv_run, alpha, B.vh.x * ((pr[0] + pr[1]) + (pr[2] + pr[3])));
         m_run = m_new;
         // rescale the accumulators of every stream whose max moved
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f && c < GS) != 0) {
@@ -785,7 +856,8 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
                 }
 #pragma unroll
                 for (int h = 0; h < GS; ++h) {
-                    const float ph = row_bcast(pr[i], h);
+                    float ph = row_bcast(pr[i], h);
+                    if constexpr (I8) ph *= B.vh.z;          // value = min + step * code
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
                 }
@@ -831,9 +903,11 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
         s_l[srow][c] = l_run;
     }
 #pragma unroll
-    for (int h = 0; h < GS; ++h)
+    for (int h = 0; h < GS; ++h) {
+        const float mh = I8 ? row_bcast(mv_run, h) : 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_o[srow][h][c * 8 + e] = acc[h][e];
+        for (int e = 0; e < 8; ++e) s_o[srow][h][c * 8 + e] = acc[h][e] + mh;
+    }
     __syncthreads();
     float vscale = 1.0f;
     if constexpr (KDT == DT_FP8) vscale = p.v_scale[g];
@@ -978,6 +1052,8 @@ KernelFn pick_partition(int kdt, int qdt, int D, int gs) {
         if (kdt == DT_BF16 && qdt == DT_BF16) return pick_gqa<DT_BF16, DT_BF16>(gs);
         if (kdt == DT_FP8 && qdt == DT_BF16) return pick_gqa<DT_FP8, DT_BF16>(gs);
         if (kdt == DT_FP8 && qdt == DT_F16) return pick_gqa<DT_FP8, DT_F16>(gs);
+        if (kdt == DT_INT8 && qdt == DT_BF16) return pick_gqa<DT_INT8, DT_BF16>(gs);
+        if (kdt == DT_INT8 && qdt == DT_F16) return pick_gqa<DT_INT8, DT_F16>(gs);
     }
     return pick_vector(kdt, qdt, D, gs);
 }
@@ -988,6 +1064,8 @@ KernelFn pick_vector(int kdt, int qdt, int D, int gs) {
     if (kdt == DT_BF16 && qdt == DT_BF16) return pick_d<DT_BF16, DT_BF16>(D, gs);
     if (kdt == DT_FP8 && qdt == DT_BF16) return pick_d<DT_FP8, DT_BF16>(D, gs);
     if (kdt == DT_FP8 && qdt == DT_F16) return pick_d<DT_FP8, DT_F16>(D, gs);
+    if (kdt == DT_INT8 && qdt == DT_BF16) return pick_d<DT_INT8, DT_BF16>(D, gs);
+    if (kdt == DT_INT8 && qdt == DT_F16) return pick_d<DT_INT8, DT_F16>(D, gs);
     return nullptr;
 }
 

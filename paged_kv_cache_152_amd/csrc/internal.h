@@ -13,9 +13,17 @@ constexpr int kZeroTileBytes = kBlock * 128 * 2;   // one 16-token tile of the w
 constexpr int kDecodeWaves = 4;   // waves per decode workgroup
 constexpr int kMaxGroupPerWg = 8; // query heads one decode workgroup serves
 
-enum Dt : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+enum Dt : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_INT8 = 4 };
 
-inline int elem_bytes(int32_t dt) { return dt == DT_F32 ? 4 : (dt == DT_FP8 ? 1 : 2); }
+__host__ __device__ inline int elem_bytes(int32_t dt) { return dt == DT_F32 ? 4 : (dt == DT_FP8 || dt == DT_INT8 ? 1 : 2); }
+
+// INT8 min-max tiles end in a 16-byte header {min, max, step = (max - min) / 255, 0}.
+constexpr int kInt8HeaderBytes = 16;
+
+// Bytes of one (block, KV head) tile of a pool.
+__host__ __device__ inline int64_t tile_bytes(int32_t dt, int32_t D) {
+    return (int64_t)kBlock * D * elem_bytes(dt) + (dt == DT_INT8 ? kInt8HeaderBytes : 0);
+}
 
 struct AppendParams {
     const int32_t* slots;
@@ -28,6 +36,8 @@ struct AppendParams {
     int64_t num_slots;    // num_blocks * kBlock
     int32_t T, H_kv, D;
     int32_t src_dt, dst_dt;
+    uint64_t* tags;       // INT8 pools: per slot (call epoch << 32 | token) of the last call that wrote it
+    uint32_t epoch;       // INT8 pools: this call's epoch (never 0)
 };
 
 constexpr int kMaxCopiesPerLaunch = 128;

@@ -76,6 +76,8 @@ struct kv_pool {
     void* v_pool = nullptr;
     float* scales = nullptr;   // device: k_scale[H], v_scale[H], k_inv[H], v_inv[H]
     void* zero_tile = nullptr; // device: kZeroTileBytes of zeros (paged_prefill reads absent tokens here)
+    uint64_t* tags = nullptr;  // device, INT8 pools: per slot, (call epoch << 32 | token) of its last append
+    uint32_t epoch = 0;        // INT8 pools: epoch of the last append call
     uint64_t pool_bytes = 0, block_bytes = 0;
     int32_t partition_tokens = 0;
 
@@ -108,7 +110,7 @@ struct kv_pool {
 
 namespace {
 
-bool dtype_known(int32_t dt) { return dt >= PKV_F32 && dt <= PKV_FP8_E4M3; }
+bool dtype_known(int32_t dt) { return dt >= PKV_F32 && dt <= PKV_INT8_MINMAX; }
 
 int elem_of(int32_t dt) { return pkv::elem_bytes(dt); }
 
@@ -185,7 +187,7 @@ int create_common(int32_t num_blocks, int32_t block_size, int32_t kv_heads, int3
     p->dtype = dtype;
     p->elem = elem_of(dtype);
     p->host_only = host_only;
-    p->block_bytes = (uint64_t)block_size * head_dim * p->elem;
+    p->block_bytes = (uint64_t)pkv::tile_bytes(dtype, head_dim);
     p->pool_bytes = (uint64_t)num_blocks * kv_heads * p->block_bytes;
     p->free_list.assign(ord.begin(), ord.end());
     p->ref.assign(num_blocks, 0);
@@ -197,6 +199,10 @@ int create_common(int32_t num_blocks, int32_t block_size, int32_t kv_heads, int3
         if (e == hipSuccess) e = hipMemset(p->v_pool, 0, p->pool_bytes);
         if (e == hipSuccess) e = hipMalloc(&p->zero_tile, pkv::kZeroTileBytes);
         if (e == hipSuccess) e = hipMemset(p->zero_tile, 0, pkv::kZeroTileBytes);
+        if (e == hipSuccess && dtype == PKV_INT8_MINMAX) {
+            e = hipMalloc(&p->tags, sizeof(uint64_t) * num_blocks * block_size);
+            if (e == hipSuccess) e = hipMemset(p->tags, 0, sizeof(uint64_t) * num_blocks * block_size);
+        }
         if (e == hipSuccess && dtype == PKV_FP8_E4M3) {
             e = hipMalloc(&p->scales, sizeof(float) * 4 * kv_heads);
             if (e == hipSuccess) {
@@ -313,6 +319,7 @@ int kv_pool_destroy(kv_pool_t* pool) {
         if (pool->v_pool) hipFree(pool->v_pool);
         if (pool->scales) hipFree(pool->scales);
         if (pool->zero_tile) hipFree(pool->zero_tile);
+        if (pool->tags) hipFree(pool->tags);
         if (pool->staging) hipFree(pool->staging);
     }
     delete pool;
@@ -330,7 +337,8 @@ int kv_pool_info(const kv_pool_t* p, kv_pool_info_t* out) {
     out->block_bytes = p->block_bytes;
     out->total_bytes = p->host_only ? 0
                                     : 2 * p->pool_bytes + (p->scales ? 4ull * sizeof(float) * p->kv_heads : 0) +
-                                          (uint64_t)pkv::kZeroTileBytes;
+                                          (uint64_t)pkv::kZeroTileBytes +
+                                          (p->tags ? sizeof(uint64_t) * p->num_blocks * p->block_size : 0);
     out->num_blocks = p->num_blocks;
     out->block_size = p->block_size;
     out->kv_heads = p->kv_heads;
@@ -721,8 +729,10 @@ int kv_append(kv_pool_t* p, const int32_t* slot_mapping, int32_t T, const void* 
     if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
     if (T < 0) return fail(PKV_ERR_INVALID_ARG, "T < 0");
     if (!dtype_known(src_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown src dtype %d", src_dtype);
-    const bool pairing = src_dtype == p->dtype ||
-                         (p->dtype == PKV_FP8_E4M3 && (src_dtype == PKV_BF16 || src_dtype == PKV_F32));
+    const bool pairing = (src_dtype == p->dtype && p->dtype != PKV_INT8_MINMAX) ||
+                         (p->dtype == PKV_FP8_E4M3 && (src_dtype == PKV_BF16 || src_dtype == PKV_F32)) ||
+                         (p->dtype == PKV_INT8_MINMAX &&
+                          (src_dtype == PKV_BF16 || src_dtype == PKV_F16 || src_dtype == PKV_F32));
     if (!pairing) return fail(PKV_ERR_UNSUPPORTED, "cannot append dtype %d into a pool of dtype %d", src_dtype, p->dtype);
     if (T > 0 && (!slot_mapping || !k_new || !v_new)) return fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
     if (T > 0 && (!aligned16(k_new) || !aligned16(v_new))) return fail(PKV_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
@@ -743,6 +753,11 @@ int kv_append(kv_pool_t* p, const int32_t* slot_mapping, int32_t T, const void* 
     a.D = p->head_dim;
     a.src_dt = src_dtype;
     a.dst_dt = p->dtype;
+    if (p->tags) {
+        if (++p->epoch == 0) ++p->epoch;      // 0 marks a slot never written
+        a.tags = p->tags;
+        a.epoch = p->epoch;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int rc = flush_copies(p, s);       // copy-on-write before the new rows land
     if (rc != PKV_OK) return rc;

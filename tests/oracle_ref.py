@@ -50,7 +50,7 @@ def expected(w: wl.Workload, seqs=None, step: int = 0, lens_override=None, nthre
                                    np.array(ln, np.int32), w.scale, nthreads=nthreads, **kw)
 
 
-TOL = {wl.F32: 1e-4, wl.F16: 5e-3, wl.BF16: 5e-3, wl.E4M3: 1e-2}
+TOL = {wl.F32: 1e-4, wl.F16: 5e-3, wl.BF16: 5e-3, wl.E4M3: 1e-2, wl.INT8: 5e-3}
 _FRAC_BITS = {wl.F32: 23, wl.F16: 10, wl.BF16: 7}
 _MIN_EXP = {wl.F32: -126, wl.F16: -14, wl.BF16: -126}
 

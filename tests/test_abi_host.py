@@ -234,6 +234,36 @@ def test_pool_info_bytes():
         p.close()
 
 
+def test_int8_pool_layout_and_pairings():
+    """INT8 min-max pools: a tile is 16 x head_dim codes plus a 16-byte header;
+    appends take BF16 / F16 / F32 sources only; decode takes BF16 or F16
+    queries; prefill has no INT8 kernel; FP8 scales do not apply."""
+    L = pkv.lib()
+    for D in (16, 64, 128):
+        p = pkv.KVPool(10, 8, D, pkv.INT8_MINMAX, host_only=True)
+        inf = p.info()
+        assert inf["block_bytes"] == 16 * D + 16 and inf["elem_bytes"] == 1
+        assert inf["pool_bytes"] == 10 * 8 * (16 * D + 16)
+        p.close()
+    p = pkv.KVPool(8, 2, 128, pkv.INT8_MINMAX, host_only=True)
+    h = p.handle
+    fake = ctypes.c_void_p(0x10000)     # never dereferenced: every call below is refused on the host
+    ap = lambda dt: L.kv_append(h, fake, 3, fake, fake, dt, None)
+    for dt in (pkv.BF16, pkv.F16, pkv.F32):
+        assert ap(dt) == pkv.ERR_STATE                 # accepted pairing; host-only pool
+    for dt in (pkv.FP8_E4M3, pkv.INT8_MINMAX):
+        assert ap(dt) == pkv.ERR_UNSUPPORTED
+    dec = lambda qdt: L.paged_decode(h, fake, qdt, 2, 8, fake, 4, fake, 64, 0.125, fake, None, 0, None)
+    assert dec(pkv.BF16) == pkv.ERR_STATE and dec(pkv.F16) == pkv.ERR_STATE
+    assert dec(pkv.F32) == pkv.ERR_UNSUPPORTED
+    pre = L.paged_prefill(h, fake, pkv.BF16, 1, 8, fake, 4, 4, fake, 4, fake, 0.1, 1, fake, None)
+    assert pre == pkv.ERR_UNSUPPORTED
+    with pytest.raises(pkv.PagedKVError) as e:
+        p.set_fp8_scales([1.0, 1.0], [1.0, 1.0])
+    assert e.value.code == pkv.ERR_STATE
+    p.close()
+
+
 def test_fp8_scale_validation():
     p = pkv.KVPool(4, 2, 128, pkv.FP8_E4M3, host_only=True)
     p.set_fp8_scales([0.5, 0.25], [1.0, 2.0])

@@ -1,0 +1,223 @@
+"""INT8 per-block min-max pools ([moo] www.mooersco.com/news/1484987 §3.3) on
+the GPU, through the C ABI.
+
+The oracle's tile model (oracle.int8_minmax.TileStore) is fed the same slots
+and the same source values as kv_append.  The pool's codes and the (min, max,
+step) header of every tile a sequence uses must equal the model's bit for bit;
+decode attention must match the fp64 oracle run on the values the model's codes
+stand for.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import harness
+import oracle
+import paged_kv_cache_152_amd as pkv
+import workloads as wl
+from oracle import int8_minmax as i8
+from tests.oracle_ref import TOL, parity_error
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+class Int8Case:
+    """Sequences grown by a prefill chunk and then by decode steps that append
+    one token to every live sequence per call, into an INT8 pool."""
+
+    def __init__(self, H_kv, D, lens, src_dt, seed, prefill_frac=0.5, num_blocks=None, scale_jitter=True):
+        self.rng = np.random.default_rng(seed)
+        self.H_kv, self.D, self.src_dt = H_kv, D, src_dt
+        nb = num_blocks or int(sum(-(-n // 16) for n in lens)) + 4
+        self.pool = pkv.KVPool(nb, H_kv, D, pkv.INT8_MINMAX, free_order=self.rng.permutation(nb))
+        self.model = i8.TileStore(H_kv, D)
+        self.seqs = [self.pool.seq_create() for _ in lens]
+        self.lens = list(lens)
+        self.cur = [0] * len(lens)
+        self.scale_jitter = scale_jitter
+        first = [max(1, int(n * prefill_frac)) if n > 0 else 0 for n in lens]
+        for i, n in enumerate(first):                         # one call per sequence
+            if n:
+                self.append([i], n)
+        while any(c < n for c, n in zip(self.cur, self.lens)):   # decode steps: one call per step
+            live = [i for i, (c, n) in enumerate(zip(self.cur, self.lens)) if c < n]
+            self.append(live, 1)
+
+    def _values(self, n):
+        x = self.rng.standard_normal((n, self.H_kv, self.D)).astype(np.float32)
+        if self.scale_jitter:                                # some tokens widen the range
+            x *= self.rng.choice(np.array([0.5, 1.0, 1.0, 2.5], np.float32), size=(n, 1, 1))
+        return wl.cast_to_storage(x, self.src_dt)
+
+    def append(self, which, n_each):
+        slots, Ks, Vs = [], [], []
+        for i in which:
+            slots.append(self.pool.seq_reserve(self.seqs[i], n_each))
+            Ks.append(self._values(n_each))
+            Vs.append(self._values(n_each))
+            self.cur[i] += n_each
+        slots = np.concatenate(slots)
+        K, V = np.concatenate(Ks), np.concatenate(Vs)
+        self.pool.append(torch.from_numpy(slots).cuda(), harness.to_device(K, self.src_dt),
+                         harness.to_device(V, self.src_dt))
+        self.model.append(slots, wl.storage_to_f32(K, self.src_dt), wl.storage_to_f32(V, self.src_dt))
+
+    def tables(self, seqs=None):
+        seqs = self.seqs if seqs is None else seqs
+        mb = max(1, max(-(-self.pool.seq_length(s) // 16) for s in seqs))
+        return self.pool.block_tables(seqs, mb)
+
+    def check_tiles(self):
+        """Codes of every live row and every used tile's header, bit for bit."""
+        kpool, vpool = self.pool.copy_to_host()
+        tb = self.pool.info()["block_bytes"]
+        assert tb == 16 * self.D + 16
+        tables, lens = self.tables()
+        n_rows = 0
+        for kind, raw in (("k", kpool), ("v", vpool)):
+            for s, n in enumerate(lens):
+                for j in range(-(-int(n) // 16)):
+                    blk = int(tables[s, j])
+                    rows = min(16, int(n) - 16 * j)
+                    for g in range(self.H_kv):
+                        t0 = (blk * self.H_kv + g) * tb
+                        codes = raw[t0:t0 + 16 * self.D].reshape(16, self.D)
+                        header = raw[t0 + 16 * self.D:t0 + tb].view(np.float32)
+                        want_codes, (lo, hi) = self.model.tile(kind, blk, g)
+                        assert np.array_equal(codes[:rows], want_codes[:rows]), (kind, s, j, g)
+                        assert header[0] == lo and header[1] == hi, (kind, s, j, g, header[:2], lo, hi)
+                        assert header[2] == i8.step(lo, hi), (kind, s, j, g)
+                        n_rows += rows
+        return n_rows
+
+    def expected(self, q, q_dt, scale, seqs=None):
+        idx = list(range(len(self.seqs))) if seqs is None else seqs
+        tables, lens = self.tables([self.seqs[i] for i in idx])
+        Ks, Vs, off, t = [], [], [], 0
+        for s, n in enumerate(lens):
+            Ks.append(self.model.values("k", tables[s], int(n)))
+            Vs.append(self.model.values("v", tables[s], int(n)))
+            off.append(t)
+            t += int(n)
+        K = np.concatenate(Ks) if t else np.zeros((0, self.H_kv, self.D))
+        V = np.concatenate(Vs) if t else np.zeros((0, self.H_kv, self.D))
+        return oracle.decode_attention(q, q_dt, K, V, oracle.F64, np.array(off), np.array(lens), scale)
+
+    def decode(self, q, q_dt, scale, seqs=None):
+        idx = list(range(len(self.seqs))) if seqs is None else seqs
+        tables, lens = self.tables([self.seqs[i] for i in idx])
+        out = self.pool.decode(harness.to_device(q, q_dt), torch.from_numpy(tables).cuda(),
+                               torch.from_numpy(lens).cuda(), int(lens.max()), scale)
+        torch.cuda.synchronize()
+        return harness.out_to_f64(out)
+
+    def query(self, B, H_q, q_dt, seed):
+        r = np.random.default_rng(seed)
+        return wl.cast_to_storage(r.standard_normal((B, H_q, self.D)).astype(np.float32), q_dt)
+
+
+@pytest.mark.parametrize("src_dt", [wl.BF16, wl.F16, wl.F32])
+@pytest.mark.parametrize("D", [16, 64, 128])
+def test_int8_append_codes_bit_exact(src_dt, D):
+    c = Int8Case(2, D, [1, 15, 16, 17, 40, 77], src_dt, seed=100 + D + src_dt)
+    rows = c.check_tiles()
+    say(f"int8 append D={D} src={src_dt}: {rows} rows bit-exact")
+    c.pool.close()
+
+
+@pytest.mark.parametrize("q_dt", [wl.BF16, wl.F16])
+@pytest.mark.parametrize("D,G", [(128, 1), (128, 2), (128, 4), (128, 8), (64, 1), (64, 5), (16, 3)])
+def test_int8_decode_vs_oracle(q_dt, D, G):
+    H_kv = 2
+    c = Int8Case(H_kv, D, [1, 37, 130, 300, 16, 0], wl.BF16, seed=200 + D + G + q_dt)
+    q = c.query(len(c.seqs), G * H_kv, q_dt, seed=7 + G)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    got, want = c.decode(q, q_dt, scale), c.expected(q, q_dt, scale)
+    assert np.isfinite(got).all()
+    err = parity_error(got, want, q_dt)
+    say(f"int8 decode D={D} G={G} q={q_dt}: err {err:.2e}")
+    assert err <= TOL[wl.INT8]
+    c.pool.close()
+
+
+def test_int8_many_partitions():
+    """Long contexts: the planned multi-partition path (work list + merge)."""
+    c = Int8Case(2, 128, [9000, 5000, 700, 6100], wl.BF16, seed=300, prefill_frac=0.99)
+    c.pool.set_partition(512)
+    for G in (1, 4):
+        q = c.query(4, 2 * G, wl.BF16, seed=301 + G)
+        scale = float(np.float32(1 / math.sqrt(128)))
+        err = parity_error(c.decode(q, wl.BF16, scale), c.expected(q, wl.BF16, scale), wl.BF16)
+        say(f"int8 long contexts G={G}: err {err:.2e}")
+        assert err <= TOL[wl.INT8]
+    c.check_tiles()
+    c.pool.close()
+
+
+def test_int8_fork_copy_on_write():
+    """A fork inside a block: the child's first append copies the block (codes
+    and header) and then widens / re-encodes the copy; the parent's tile stays."""
+    c = Int8Case(2, 64, [40], wl.BF16, seed=400, prefill_frac=1.0)
+    parent = c.seqs[0]
+    before_tables, _ = c.tables()
+    child = c.pool.seq_fork(parent, 40)
+    c.seqs.append(child)
+    c.lens.append(41)
+    c.cur.append(40)
+    shared = int(before_tables[0, 2])                 # block holding rows 32..39
+    K = wl.cast_to_storage(3 * c.rng.standard_normal((1, 2, 64)).astype(np.float32), wl.BF16)
+    slots = c.pool.seq_reserve(child, 1)
+    c.pool.append(torch.from_numpy(slots).cuda(), harness.to_device(K, wl.BF16), harness.to_device(K, wl.BF16))
+    copy = int(slots[0]) // 16
+    assert copy != shared
+    c.model.copy_block(shared, copy)
+    c.model.append(slots, wl.storage_to_f32(K, wl.BF16), wl.storage_to_f32(K, wl.BF16))
+    c.check_tiles()
+    q = c.query(2, 4, wl.BF16, seed=401)
+    scale = 0.125
+    err = parity_error(c.decode(q, wl.BF16, scale), c.expected(q, wl.BF16, scale), wl.BF16)
+    assert err <= TOL[wl.INT8]
+    c.pool.close()
+
+
+def test_int8_swap_round_trip():
+    """Swap-out and back: the tiles (codes and headers) move whole, so decode is
+    bit-identical and every tile equals the model's once its blocks are renamed."""
+    c = Int8Case(2, 128, [100, 33], wl.BF16, seed=500)
+    q = c.query(2, 8, wl.BF16, seed=501)
+    before = c.decode(q, wl.BF16, 0.09)
+    old, _ = c.tables()
+    host = c.pool.swap_out(c.seqs[0])
+    assert host.numel() == c.pool.swap_bytes(c.seqs[0]) == 7 * 2 * 2 * (16 * 128 + 16)
+    c.pool.swap_in(c.seqs[0], host)
+    new, _ = c.tables()
+    moved = [(int(a), int(b)) for a, b in zip(old[0][:7], new[0][:7])]
+    snap = {(kind, a, g): c.model.tile(kind, a, g) for a, _ in moved for kind in "kv" for g in range(2)}
+    for a, b in moved:
+        for kind in "kv":
+            for g in range(2):
+                codes, rng = snap[(kind, a, g)]
+                c.model.codes[(kind, b, g)] = codes.copy()
+                c.model.range[(kind, b, g)] = rng
+    c.check_tiles()
+    assert np.array_equal(before, c.decode(q, wl.BF16, 0.09))
+    c.pool.close()
+
+
+def test_int8_prefill_unsupported():
+    c = Int8Case(2, 128, [20], wl.BF16, seed=600)
+    tables, lens = c.tables()
+    q = torch.zeros((4, 4, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(pkv.PagedKVError) as e:
+        c.pool.prefill(q, torch.tensor([0, 4], dtype=torch.int32, device="cuda"), torch.from_numpy(tables).cuda(),
+                       torch.from_numpy(lens).cuda(), 4, 0.1)
+    assert e.value.code == pkv.ERR_UNSUPPORTED
+    c.pool.close()

@@ -35,11 +35,18 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-F32, F16, BF16, E4M3 = 0, 1, 2, 3
+F32, F16, BF16, E4M3, INT8 = 0, 1, 2, 3, 4
 BLOCK = 16
-_NP = {F32: np.float32, F16: np.float16, BF16: np.uint16, E4M3: np.uint8}
-ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}
-DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", E4M3: "fp8_e4m3"}
+_NP = {F32: np.float32, F16: np.float16, BF16: np.uint16, E4M3: np.uint8, INT8: np.uint8}
+ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1, INT8: 1}
+DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", E4M3: "fp8_e4m3", INT8: "int8_minmax"}
+
+
+def storage_to_f32(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact float32 values of f32 / f16 / bf16 (uint16 bits) storage."""
+    if dtype == BF16:
+        return bf16_bits_to_f32(x)
+    return np.asarray(x, dtype=_NP[dtype]).astype(np.float32)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
