@@ -106,11 +106,10 @@ def cpu_baseline(w: wl.Workload, budget_s: float = 15.0):
     The oracle spreads (sequence, KV head) pairs over its threads, so each call
     gets enough sequences to give every thread at least two pairs."""
     import oracle
-    from tests.oracle_ref import fp8_codes
+    from tests.oracle_ref import fp8_codes, int8_values
     order = np.random.default_rng(0).permutation(w.B)
     threads = oracle.num_threads()
     group = max(1, min(w.B, -(-2 * threads // w.H_kv)))
-    per_tok = w.H_kv * w.D * 2 * wl.ELEM_BYTES[w.kv_dtype]
     scales = w.fp8_scales()
     kw = dict(k_scale=scales[0], v_scale=scales[1]) if scales else {}
     q_all = w.q()
@@ -118,10 +117,14 @@ def cpu_baseline(w: wl.Workload, budget_s: float = 15.0):
     # one seeded group of sequences, generated once (not timed), decoded repeatedly
     seqs = [int(b) for b in order[:group]]
     Ks, Vs, offs, ns, off = [], [], [], [], 0
+    kv_code = oracle.F64 if w.kv_dtype == wl.INT8 else w.kv_dtype
     for b in seqs:
-        K, V = w.kv(b)
         n = int(lens[b])
-        K, V = K[:n], V[:n]
+        if w.kv_dtype == wl.INT8:            # the values the pool's codes stand for
+            K, V = int8_values(w, b, n)
+        else:
+            K, V = w.kv(b)
+            K, V = K[:n], V[:n]
         if w.kv_dtype == wl.E4M3:
             K, V = fp8_codes(K, scales[0]), fp8_codes(V, scales[1])
         Ks.append(K)
@@ -134,10 +137,10 @@ def cpu_baseline(w: wl.Workload, budget_s: float = 15.0):
     done_time, calls = 0.0, 0
     while done_time < budget_s:
         t0 = time.perf_counter()
-        oracle.decode_attention(q, w.q_dtype, K, V, w.kv_dtype, offs, ns, w.scale, **kw)
+        oracle.decode_attention(q, w.q_dtype, K, V, kv_code, offs, ns, w.scale, **kw)
         done_time += time.perf_counter() - t0
         calls += 1
-    done_bytes = calls * sum(ns) * per_tok
+    done_bytes = calls * w.kv_bytes(ns)
     return {"value": round(done_bytes / done_time / 1e9, 4), "unit": "GB/s",
             "cores": min(threads, group * w.H_kv), "kind": "oracle",
             "sample": f"fp64 oracle, {calls} calls each decoding the same {group} of the {w.B} sequences "
@@ -325,7 +328,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8", "prefill8b", "swap"])
+    ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8", "int8", "prefill8b", "swap"])
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)

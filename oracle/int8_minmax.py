@@ -40,55 +40,61 @@ BLOCK = 16
 
 
 def encode(x, k_min, k_max) -> np.ndarray:
-    """Codes of fp32 values under the range (k_min, k_max) (R2)."""
+    """Codes of fp32 values under the range (k_min, k_max) (R2); k_min and
+    k_max may be arrays that broadcast against x."""
     x = np.asarray(x, dtype=np.float32)
-    lo, hi = F32(k_min), F32(k_max)
-    if not hi > lo:
-        return np.zeros(x.shape, dtype=np.uint8)
-    with np.errstate(invalid="ignore", over="ignore"):
-        d = x - lo                              # fp32
-        t = d / (hi - lo)                       # fp32, correctly rounded division
-        c = np.rint(t * F32(255))               # fp32 product, round half to even
+    lo, hi = np.asarray(k_min, dtype=np.float32), np.asarray(k_max, dtype=np.float32)
+    ok = hi > lo
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        d = x - lo                                              # fp32
+        t = d / np.where(ok, hi - lo, np.float32(1))            # fp32, correctly rounded division
+        c = np.rint(t * F32(255))                               # fp32 product, round half to even
     c = np.where(np.isnan(c), F32(0), np.clip(c, F32(0), F32(255)))
-    return c.astype(np.uint8)
+    return np.where(ok, c, F32(0)).astype(np.uint8)
 
 
-def step(k_min, k_max) -> np.float32:
+def step(k_min, k_max):
     """(k_max - k_min) / 255 in fp32."""
-    return F32(F32(k_max) - F32(k_min)) / F32(255)
+    return (np.asarray(k_max, dtype=np.float32) - np.asarray(k_min, dtype=np.float32)) / F32(255)
 
 
 def value_f32(codes, k_min, k_max) -> np.ndarray:
     """fp32 value of codes, as a re-encode reads it (R4): k_min + code * step."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.float32)
-    return F32(k_min) + c * step(k_min, k_max)
+    return np.asarray(k_min, dtype=np.float32) + c * step(k_min, k_max)
 
 
 def value(codes, k_min, k_max) -> np.ndarray:
     """The value a code stands for (R3), in fp64."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.float64)
-    lo, hi = float(F32(k_min)), float(F32(k_max))
+    lo = np.asarray(k_min, dtype=np.float32).astype(np.float64)
+    hi = np.asarray(k_max, dtype=np.float32).astype(np.float64)
     # = lo + c (hi - lo) / 255; both products are exact in fp64, so codes 0 and
     # 255 give k_min and k_max exactly
     return (lo * (255.0 - c) + hi * c) / 255.0
 
 
 class TileStore:
-    """The INT8 pool as appends leave it: per (tensor, block, KV head) a tile of
-    16 rows of head_dim codes and its range (R1, R4).  Keys are physical
-    block ids, so the model follows the same slots as the library."""
+    """The INT8 pool as appends leave it: per (tensor, block) the tiles of all
+    KV heads -- codes [H_kv][16][D] and ranges lo, hi [H_kv] (R1, R4).  Keys
+    are physical block ids, so the model follows the same slots as the
+    library.  Each head's tile is handled on its own; the heads of one block
+    are only evaluated together."""
 
     def __init__(self, H_kv: int, D: int):
         self.H_kv, self.D = H_kv, D
-        self.codes: dict = {}
-        self.range: dict = {}
+        self.blocks: dict = {}
+
+    def _block(self, kind: str, block: int):
+        b = self.blocks.get((kind, block))
+        if b is None:
+            b = (np.zeros((self.H_kv, BLOCK, self.D), dtype=np.uint8),
+                 np.zeros(self.H_kv, dtype=np.float32), np.zeros(self.H_kv, dtype=np.float32))
+        return b
 
     def tile(self, kind: str, block: int, head: int):
-        key = (kind, block, head)
-        codes = self.codes.get(key)
-        if codes is None:
-            codes = np.zeros((BLOCK, self.D), dtype=np.uint8)
-        return codes, self.range.get(key, (F32(0), F32(0)))
+        codes, lo, hi = self._block(kind, block)
+        return codes[head], (lo[head], hi[head])
 
     def append(self, slots, K, V) -> None:
         """One append call: token t goes to slot slots[t] (block slot // 16, row
@@ -104,40 +110,34 @@ class TileStore:
             assert s % BLOCK not in rows, "duplicate slot in one call"
             rows[s % BLOCK] = t
         for block, rows in rows_of.items():
-            for g in range(self.H_kv):
-                self._write("k", block, g, {r: K[t, g] for r, t in rows.items()})
-                self._write("v", block, g, {r: V[t, g] for r, t in rows.items()})
+            r = np.array(sorted(rows))
+            t = np.array([rows[i] for i in r.tolist()])
+            self._write("k", block, r, K[t].transpose(1, 0, 2))
+            self._write("v", block, r, V[t].transpose(1, 0, 2))
 
-    def _write(self, kind: str, block: int, head: int, new: dict) -> None:
-        codes, (old_lo, old_hi) = self.tile(kind, block, head)
-        codes = codes.copy()
-        vals = np.stack(list(new.values()))
-        lo, hi = F32(np.min(vals)), F32(np.max(vals))
-        if 0 not in new:                        # the tile continues: widen, re-encode the rest
-            lo, hi = min(old_lo, lo), max(old_hi, hi)
-            if (lo, hi) != (old_lo, old_hi):
-                rest = [r for r in range(BLOCK) if r not in new]
-                codes[rest] = encode(value_f32(codes[rest], old_lo, old_hi), lo, hi)
-        for r, x in new.items():
-            codes[r] = encode(x, lo, hi)
-        self.codes[(kind, block, head)] = codes
-        self.range[(kind, block, head)] = (F32(lo), F32(hi))
+    def _write(self, kind: str, block: int, rows: np.ndarray, new: np.ndarray) -> None:
+        """Rows `rows` of every head's tile get new[h] ([H_kv][len(rows)][D])."""
+        codes, old_lo, old_hi = (a.copy() for a in self._block(kind, block))
+        lo, hi = new.min(axis=(1, 2)), new.max(axis=(1, 2))
+        if 0 not in rows:                       # the tile continues: widen, re-encode the rest
+            lo, hi = np.minimum(old_lo, lo), np.maximum(old_hi, hi)
+            rest = np.setdiff1d(np.arange(BLOCK), rows)
+            for h in np.flatnonzero((lo != old_lo) | (hi != old_hi)):
+                codes[h, rest] = encode(value_f32(codes[h, rest], old_lo[h], old_hi[h]), lo[h], hi[h])
+        codes[:, rows] = encode(new, lo[:, None, None], hi[:, None, None])
+        self.blocks[(kind, block)] = (codes, lo.astype(np.float32), hi.astype(np.float32))
 
     def copy_block(self, src: int, dst: int) -> None:
         """A whole-block copy (copy-on-write, swap): codes and ranges move alike."""
         for kind in ("k", "v"):
-            for g in range(self.H_kv):
-                codes, rng = self.tile(kind, src, g)
-                self.codes[(kind, dst, g)] = codes.copy()
-                self.range[(kind, dst, g)] = rng
+            self.blocks[(kind, dst)] = tuple(a.copy() for a in self._block(kind, src))
 
     def values(self, kind: str, blocks, n: int) -> np.ndarray:
         """fp64 values [n][H_kv][D] of the first n tokens of a sequence whose
         block table starts with `blocks` (R3)."""
         out = np.empty((n, self.H_kv, self.D), dtype=np.float64)
-        for j in range(n):
-            b, r = blocks[j // BLOCK], j % BLOCK
-            for g in range(self.H_kv):
-                codes, (lo, hi) = self.tile(kind, b, g)
-                out[j, g] = value(codes[r], lo, hi)
+        for j in range(-(-n // BLOCK)):
+            codes, lo, hi = self._block(kind, int(blocks[j]))
+            rows = min(BLOCK, n - BLOCK * j)
+            out[BLOCK * j:BLOCK * j + rows] = value(codes[:, :rows], lo[:, None, None], hi[:, None, None]).transpose(1, 0, 2)
         return out

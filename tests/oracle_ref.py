@@ -21,6 +21,27 @@ def fp8_codes(x_bf16_bits: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return oracle.e4m3_encode(x.astype(np.float32))
 
 
+APPEND_CHUNK_TOKENS = 1 << 16      # the harness appends a prefill in calls of this many tokens
+
+
+def int8_values(w: wl.Workload, b: int, n: int):
+    """fp64 values [n][H_kv][D] of sequence b's K and V in an INT8 pool, from the
+    oracle's tile model fed the same append calls the harness makes: the
+    prefill in chunks, then the decode step's token on its own."""
+    from oracle import int8_minmax as i8
+    K, V = w.kv(b)
+    K, V = wl.storage_to_f32(K[:n], w.src_dtype), wl.storage_to_f32(V[:n], w.src_dtype)
+    store = i8.TileStore(w.H_kv, w.D)
+    n_pre = min(n, int(w.prefill[b]))
+    for s in range(0, n_pre, APPEND_CHUNK_TOKENS):
+        e = min(n_pre, s + APPEND_CHUNK_TOKENS)
+        store.append(np.arange(s, e), K[s:e], V[s:e])
+    for t in range(n_pre, n):
+        store.append(np.array([t]), K[t:t + 1], V[t:t + 1])
+    blocks = np.arange(-(-n // wl.BLOCK))
+    return store.values("k", blocks, n), store.values("v", blocks, n)
+
+
 def expected(w: wl.Workload, seqs=None, step: int = 0, lens_override=None, nthreads: int = 0):
     """fp64 oracle output [len(seqs)][H_q][D] for the given sequence indices."""
     seqs = list(range(w.B)) if seqs is None else list(seqs)
@@ -28,10 +49,14 @@ def expected(w: wl.Workload, seqs=None, step: int = 0, lens_override=None, nthre
     Ks, Vs, off, ln = [], [], [], []
     t = 0
     scales = w.fp8_scales()
+    kv_code = oracle.F64 if w.kv_dtype == wl.INT8 else w.kv_dtype
     for b in seqs:
         n = int(lens[b])
-        K, V = w.kv(b)
-        K, V = K[:n], V[:n]
+        if w.kv_dtype == wl.INT8:
+            K, V = int8_values(w, b, n)
+        else:
+            K, V = w.kv(b)
+            K, V = K[:n], V[:n]
         if w.kv_dtype == wl.E4M3:
             K, V = fp8_codes(K, scales[0]), fp8_codes(V, scales[1])
         Ks.append(K)
@@ -40,13 +65,14 @@ def expected(w: wl.Workload, seqs=None, step: int = 0, lens_override=None, nthre
         ln.append(n)
         t += n
     shape = (0, w.H_kv, w.D)
-    K = np.concatenate(Ks) if t else np.zeros(shape, wl._NP[w.kv_dtype])
-    V = np.concatenate(Vs) if t else np.zeros(shape, wl._NP[w.kv_dtype])
+    empty = np.float64 if w.kv_dtype == wl.INT8 else wl._NP[w.kv_dtype]
+    K = np.concatenate(Ks) if t else np.zeros(shape, empty)
+    V = np.concatenate(Vs) if t else np.zeros(shape, empty)
     q = w.q(step)[seqs]
     kw = {}
     if w.kv_dtype == wl.E4M3:
         kw = dict(k_scale=scales[0], v_scale=scales[1])
-    return oracle.decode_attention(q, w.q_dtype, K, V, w.kv_dtype, np.array(off, np.int64),
+    return oracle.decode_attention(q, w.q_dtype, K, V, kv_code, np.array(off, np.int64),
                                    np.array(ln, np.int32), w.scale, nthreads=nthreads, **kw)
 
 

@@ -45,9 +45,9 @@ def run_case(w, partition=0, poison=False, free_order=None):
 
 def assert_close(got, want, kv_dtype, what="", out_dtype=None):
     """max |got - want| <= TOL[kv dtype] beyond half an ulp of the output format
-    (the output is stored in the q dtype: bf16 for FP8 pools, else the KV dtype)."""
+    (the output is stored in the q dtype: bf16 for FP8 and INT8 pools, else the KV dtype)."""
     if out_dtype is None:
-        out_dtype = wl.BF16 if kv_dtype == wl.E4M3 else kv_dtype
+        out_dtype = wl.BF16 if kv_dtype in (wl.E4M3, wl.INT8) else kv_dtype
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     err = parity_error(got, want, out_dtype)
     raw = float(np.abs(got - want).max()) if got.size else 0.0
@@ -404,7 +404,7 @@ def _sample(w, k=4):
     return sorted(idx)
 
 
-@pytest.mark.parametrize("name", ["mha7b", "gqa8b", "mixed", "fp8"])
+@pytest.mark.parametrize("name", ["mha7b", "gqa8b", "mixed", "fp8", "int8"])
 def test_full_size_config_sampled(name):
     """Full-size workloads in the launch configuration the benchmark times,
     checked on sampled sequences (all their heads) against the oracle."""

@@ -68,13 +68,16 @@ I8_MUTANTS = {
                             [pins.check_int8_round_trip]),
     "int8_value_reversed": ("(lo * (255.0 - c) + hi * c) / 255.0", "(hi * (255.0 - c) + lo * c) / 255.0",
                             [pins.check_int8_round_trip]),
-    "int8_no_restart_at_row0": ("if 0 not in new:", "if True:", [pins.check_int8_fill_invariants]),
-    "int8_range_not_widened": ("lo, hi = min(old_lo, lo), max(old_hi, hi)", "lo, hi = lo, hi",
+    "int8_no_restart_at_row0": ("if 0 not in rows:", "if True:", [pins.check_int8_fill_invariants]),
+    "int8_range_not_widened": ("lo, hi = np.minimum(old_lo, lo), np.maximum(old_hi, hi)", "lo, hi = lo, hi",
                                [pins.check_int8_fill_invariants]),
-    "int8_no_reencode": ("codes[rest] = encode(value_f32(codes[rest], old_lo, old_hi), lo, hi)", "pass",
-                         [pins.check_int8_fill_invariants]),
-    "int8_reencode_reads_new_range": ("value_f32(codes[rest], old_lo, old_hi)", "value_f32(codes[rest], lo, hi)",
-                                      [pins.check_int8_fill_invariants]),
+    "int8_no_reencode": ("codes[h, rest] = encode(value_f32(codes[h, rest], old_lo[h], old_hi[h]), lo[h], hi[h])",
+                         "pass", [pins.check_int8_fill_invariants]),
+    "int8_reencode_reads_new_range": ("value_f32(codes[h, rest], old_lo[h], old_hi[h])",
+                                      "value_f32(codes[h, rest], lo[h], hi[h])", [pins.check_int8_fill_invariants]),
+    "int8_heads_share_a_range": ("lo, hi = new.min(axis=(1, 2)), new.max(axis=(1, 2))",
+                                 "lo, hi = np.full(self.H_kv, new.min()), np.full(self.H_kv, new.max())",
+                                 [pins.check_int8_fill_invariants]),
 }
 
 

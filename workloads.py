@@ -111,16 +111,25 @@ class Workload:
 
     @property
     def src_dtype(self) -> int:
-        """dtype of the K/V handed to kv_append (bf16 for an FP8 pool)."""
-        return BF16 if self.kv_dtype == E4M3 else self.kv_dtype
+        """dtype of the K/V handed to kv_append (bf16 for an FP8 or INT8 pool)."""
+        return BF16 if self.kv_dtype in (E4M3, INT8) else self.kv_dtype
 
     def step_lens(self) -> np.ndarray:
         """Context lengths during the first decode step (prefill + the new token)."""
         return np.minimum(self.lens, self.prefill + 1).astype(np.int32)
 
+    def kv_bytes(self, lens) -> int:
+        """Algorithmic K+V bytes of attending once over contexts `lens`: every live
+        element once, plus for INT8 pools each touched tile's 16-byte header."""
+        lens = np.asarray(lens).astype(np.int64)
+        n = int(lens.sum()) * self.H_kv * self.D * 2 * ELEM_BYTES[self.kv_dtype]
+        if self.kv_dtype == INT8:
+            n += int(((lens + BLOCK - 1) // BLOCK).sum()) * self.H_kv * 2 * 16
+        return n
+
     def kv_bytes_per_step(self) -> int:
-        """Algorithmic K+V bytes the first decode step reads: every live element once."""
-        return int(self.step_lens().astype(np.int64).sum()) * self.H_kv * self.D * 2 * ELEM_BYTES[self.kv_dtype]
+        """Algorithmic K+V bytes the first decode step reads."""
+        return self.kv_bytes(self.step_lens())
 
     def max_len(self) -> int:
         return int(self.lens.max()) if self.B else 0
@@ -283,6 +292,16 @@ def make(name: str) -> Workload:
                      sharers=sharers, prefix_tokens=2048)
         w.free_order = _free_order(seed, nb)
         return w
+    elif name == "int8":
+        # the fp8 workload's shape and values (same seed), stored as INT8 min-max codes
+        seed, B, Hq, Hkv, D, kvd, qd = 5, 32, 32, 8, 128, INT8, BF16
+        lens = np.full(B, 32768, np.int32)
+        nb = _pool_blocks(lens, [], 0, 1.25)
+        steps, pre = 1, lens - 1
+        w = Workload(name, seed, B, Hq, Hkv, D, kvd, qd, lens, nb, None, pre, steps,
+                     outlier_p=0.001, outlier_mult=20.0)
+        w.free_order = _free_order(seed, nb)
+        return w
     elif name == "fp8":
         seed, B, Hq, Hkv, D, kvd, qd = 5, 32, 32, 8, 128, E4M3, BF16
         lens = np.full(B, 32768, np.int32)
@@ -309,7 +328,7 @@ def custom(seed: int, lens, H_q: int, H_kv: int, D: int, kv_dtype: int, q_dtype:
     """A small workload of the same recipe with arbitrary shapes (parity sweeps)."""
     lens = np.asarray(lens, dtype=np.int32)
     if q_dtype is None:
-        q_dtype = BF16 if kv_dtype == E4M3 else kv_dtype
+        q_dtype = BF16 if kv_dtype in (E4M3, INT8) else kv_dtype
     nb = num_blocks if num_blocks is not None else max(1, _pool_blocks(np.maximum(lens, 1), [], 0, 1.25) + 2)
     w = Workload(f"custom{seed}", seed, len(lens), H_q, H_kv, D, kv_dtype, q_dtype, lens, nb,
                  _free_order(seed, nb), np.maximum(lens - 1, 0).astype(np.int32), 1,
