@@ -268,9 +268,19 @@ hipError_t timed_launch(kv_pool* p, const char* name, hipStream_t stream, F&& fn
         if (b) p->spare_events.push_back(b);
         return fn();
     }
-    hipEventRecord(a, stream);
+    if (hipEventRecord(a, stream) != hipSuccess) {   // no timing for this launch
+        ++t.dropped;
+        p->spare_events.push_back(a);
+        p->spare_events.push_back(b);
+        return fn();
+    }
     hipError_t e = fn();
-    hipEventRecord(b, stream);
+    if (hipEventRecord(b, stream) != hipSuccess) {
+        ++t.dropped;
+        p->spare_events.push_back(a);
+        p->spare_events.push_back(b);
+        return e;
+    }
     t.pending.emplace_back(a, b);
     return e;
 }
@@ -309,18 +319,16 @@ int kv_pool_create_host_only(int32_t num_blocks, int32_t block_size, int32_t kv_
 int kv_pool_destroy(kv_pool_t* pool) {
     if (!pool) return ok();
     if (!pool->host_only) {
+        // teardown: a failing release has nowhere to be reported, so errors are dropped
         for (auto& t : pool->timers)
             for (auto& ev : t.pending) {
-                hipEventDestroy(ev.first);
-                hipEventDestroy(ev.second);
+                (void)hipEventDestroy(ev.first);
+                (void)hipEventDestroy(ev.second);
             }
-        for (hipEvent_t e : pool->spare_events) hipEventDestroy(e);
-        if (pool->k_pool) hipFree(pool->k_pool);
-        if (pool->v_pool) hipFree(pool->v_pool);
-        if (pool->scales) hipFree(pool->scales);
-        if (pool->zero_tile) hipFree(pool->zero_tile);
-        if (pool->tags) hipFree(pool->tags);
-        if (pool->staging) hipFree(pool->staging);
+        for (hipEvent_t e : pool->spare_events) (void)hipEventDestroy(e);
+        for (void* mem : {pool->k_pool, pool->v_pool, static_cast<void*>(pool->scales), pool->zero_tile,
+                          static_cast<void*>(pool->tags), pool->staging})
+            if (mem) (void)hipFree(mem);
     }
     delete pool;
     return ok();
