@@ -222,3 +222,17 @@ def test_prefill_scale_sign(scale, kv_dt):
     c.scale = float(np.float32(scale))
     check(c.run(), c.expected(), kv_dt, c.q_dt, f"scale={scale}")
     c.close()
+
+
+@pytest.mark.parametrize("kv_dt,D,G", [(wl.BF16, 128, 4), (wl.F16, 128, 1), (wl.BF16, 64, 8), (wl.F16, 64, 5),
+                                       (wl.E4M3, 128, 4)])
+def test_prefill_bit_identical_across_runs(kv_dt, D, G):
+    """Five runs of the same launch give the same bits (no order or timing
+    dependence in staging, softmax or the accumulation), over contexts whose
+    last stage is partial, exactly full, or a single block."""
+    c = Case(kv_dt, 2 * G, 2, D, [(300, 100), (129, 64), (64, 64), (17, 17), (1000, 33)], seed=13 + D + G)
+    outs = [c.run() for _ in range(5)]
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"run {i} differs in {int((outs[0] != o).sum())} elements"
+    check(outs[0], c.expected(), kv_dt, c.q_dt, "deterministic case")
+    c.close()
