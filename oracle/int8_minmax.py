@@ -132,6 +132,15 @@ class TileStore:
         for kind in ("k", "v"):
             self.blocks[(kind, dst)] = tuple(a.copy() for a in self._block(kind, src))
 
+    def rename(self, pairs) -> None:
+        """Blocks that moved to new ids all at once (a swap-out and swap-in):
+        for each (old, new) the tiles held at `old` before the call are held
+        at `new` afterwards.  A new id may be another pair's old id."""
+        snap = {(kind, a): tuple(x.copy() for x in self._block(kind, a)) for a, _ in pairs for kind in ("k", "v")}
+        for a, b in pairs:
+            for kind in ("k", "v"):
+                self.blocks[(kind, b)] = snap[(kind, a)]
+
     def values(self, kind: str, blocks, n: int) -> np.ndarray:
         """fp64 values [n][H_kv][D] of the first n tokens of a sequence whose
         block table starts with `blocks` (R3)."""

@@ -199,14 +199,7 @@ def test_int8_swap_round_trip():
     assert host.numel() == c.pool.swap_bytes(c.seqs[0]) == 7 * 2 * 2 * (16 * 128 + 16)
     c.pool.swap_in(c.seqs[0], host)
     new, _ = c.tables()
-    moved = [(int(a), int(b)) for a, b in zip(old[0][:7], new[0][:7])]
-    snap = {(kind, a, g): c.model.tile(kind, a, g) for a, _ in moved for kind in "kv" for g in range(2)}
-    for a, b in moved:
-        for kind in "kv":
-            for g in range(2):
-                codes, rng = snap[(kind, a, g)]
-                c.model.codes[(kind, b, g)] = codes.copy()
-                c.model.range[(kind, b, g)] = rng
+    c.model.rename([(int(a), int(b)) for a, b in zip(old[0][:7], new[0][:7])])
     c.check_tiles()
     assert np.array_equal(before, c.decode(q, wl.BF16, 0.09))
     c.pool.close()

@@ -560,5 +560,25 @@ def test_int8_fill_invariants():
     check_int8_fill_invariants()
 
 
+def test_int8_tile_store_rename():
+    """Renaming blocks moves whole tiles at once, also when a new id is
+    another pair's old id (a swap of two ids, and a chain 1 -> 2 -> 5)."""
+    rng = np.random.default_rng(44)
+    store = _i8.TileStore(2, 16)
+    for b in (1, 2, 3):
+        K = rng.standard_normal((16, 2, 16)).astype(np.float32) * (b + 1)
+        store.append(np.arange(16) + 16 * b, K, -K)
+    snap = {(kind, b, g): store.tile(kind, b, g) for kind in "kv" for b in (1, 2, 3) for g in range(2)}
+    store.rename([(1, 2), (2, 1)])
+    store.rename([(1, 5), (3, 1)])
+    # after both calls: old 1 -> 2, old 2 -> 1 -> 5, old 3 -> 1
+    for old, new in ((1, 2), (2, 5), (3, 1)):
+        for kind in "kv":
+            for g in range(2):
+                codes, (lo, hi) = store.tile(kind, new, g)
+                want_codes, (wlo, whi) = snap[(kind, old, g)]
+                assert np.array_equal(codes, want_codes) and lo == wlo and hi == whi, (old, new, kind, g)
+
+
 def test_f64_storage_path():
     check_f64_storage_path()
