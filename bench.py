@@ -79,6 +79,33 @@ def host_alloc_us(w: wl.Workload, reps: int = 20) -> float:
     return dt * 1e6
 
 
+def per_step_us(torch, prep, out, ws, stream, n: int, mode: str) -> dict:
+    """p10 / p50 / p90 of single steps, each between its own event pair on the
+    library's stream.  Between steps, outside the events:
+      warm         nothing (the steps run back to back);
+      cold         a 1 GiB scratch buffer is written and then read, so the
+                   256 MB last-level cache (MALL) holds none of the previous
+                   step's K/V and no dirty lines;
+      after_write  the 1 GiB write alone: the step then also competes with the
+                   write-back of the dirty lines the fill left in the caches."""
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if mode != "warm" else None
+    evs = []
+    for i in range(n):
+        if mode != "warm":
+            scratch.fill_(i & 0xFF)
+        if mode == "cold":
+            scratch.sum(dtype=torch.int64)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        prep.step(out=out, workspace=ws)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    del scratch
+    return {k: round(float(np.percentile(us, q)), 2) for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+
 def copy_probe_gbs(nbytes: int = 2 << 30, reps: int = 10) -> float:
     """Practical HBM rate of a plain device copy (pkv_copy, 16-byte loads and
     stores): (bytes read + bytes written) / time, median of `reps` copies."""
@@ -327,7 +354,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first; the FP8 and INT8 workloads need about 40 and 90 to reach steady state")
     ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8", "int8", "prefill8b", "swap"])
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -389,6 +417,9 @@ def main():
     torch.cuda.synchronize()
     stats = pool.profile_read()
     pool.profile_enable(False)
+    step_dist = {m: per_step_us(torch, prep, out, ws, stream, args.steps, m) for m in ("warm", "cold", "after_write")}
+    log("[bench] per-step p10/p50/p90 (us): " +
+        ", ".join(f"{m} {d['p10']}/{d['p50']}/{d['p90']}" for m, d in step_dist.items()))
 
     kv_bytes = w.kv_bytes_per_step()
     kern = {k: {"launches": v["launches"], "avg_us": round(v["total_ms"] / max(1, v["launches"]) * 1e3, 3)}
@@ -421,6 +452,7 @@ def main():
         "pct_of_hbm_peak": round(100 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "kernels_us": kern,
         "decode_only_us": round((part_us or 0) + (red_us or 0) + plan_us, 3),
+        "step_us": step_dist,
         "host_alloc_us_per_step": round(host_alloc_us(w), 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
