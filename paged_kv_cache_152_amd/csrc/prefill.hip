@@ -145,7 +145,11 @@ constexpr int kAhead = 4;
 
 // Workgroups of one (sequence, head group) walk the same K/V; keep them on one
 // XCD (workgroups are dealt round-robin over the 8 XCDs), so its L2 serves the
-// repeats.  Logical index = xcd * (n / 8) + position on that XCD.
+// repeats.  Logical index = xcd * (n / 8) + position on that XCD.  Within a
+// (sequence, head group) the query tiles go last to first: under the causal
+// mask a later tile sees more keys, so the longest workgroups start first and
+// the shortest fill the end of the launch (4% shorter launch on a 16 x 512-token
+// chunk workload than first to last).
 __device__ __forceinline__ int64_t xcd_logical(int64_t i, int64_t n) {
     const int64_t full = n - n % 8;
     if (i >= full) return i;
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillPar
     const int64_t tiles = p.tiles;
     const int64_t n_wg = tiles * p.H_kv * subs * p.n_seqs;
     const int64_t L = xcd_logical(blockIdx.x, n_wg);
-    const int tile = (int)(L % tiles);
+    const int tile = (int)(tiles - 1 - L % tiles);          // latest (heaviest under the causal mask) first
     const int hgi = (int)((L / tiles) % ((int64_t)p.H_kv * subs));
     const int s = (int)(L / (tiles * p.H_kv * subs));
     const int g = hgi / subs;
@@ -431,12 +435,15 @@ __device__ __forceinline__ void wait_loads_then_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Plain maxima of finite-or-minus-infinity values.  Written in asm because
-// fmaxf must quiet signalling NaNs and costs an extra v_max per operand here.
+// Maxima of finite-or-minus-infinity values, as one v_maximum3_f32 (IEEE
+// maximum: no signalling-NaN quieting, so no extra instruction per operand as
+// fmaxf costs).  Never inline asm: a VALU read of a matrix-core result needs
+// wait states the hardware does not enforce, and the compiler inserts them only
+// for instructions it can see.  An asm v_max3_f32 fed straight from the Q.K^T
+// accumulators once read them before the MFMA had written them, so the block
+// max, and with it the rescale reference, varied from run to run.
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // Max across the four lanes of a row (l % 16 equal): v_permlane16_swap pairs
@@ -529,7 +536,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     const int64_t tiles = p.tiles;
     const int64_t n_wg = tiles * p.H_kv * subs * p.n_seqs;
     const int64_t L = xcd_logical(blockIdx.x, n_wg);
-    const int tile = (int)(L % tiles);
+    const int tile = (int)(tiles - 1 - L % tiles);          // latest (heaviest under the causal mask) first
     const int hgi = (int)((L / tiles) % ((int64_t)p.H_kv * subs));
     const int s = (int)(L / (tiles * p.H_kv * subs));
     const int g = hgi / subs;
