@@ -483,12 +483,14 @@ __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
 
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
-// Eight ds_read_b64_tr_b16: at a[m] and at a[m] + OFF bytes (the same rows of
-// the next block), then a wait for them.  In asm because the compiler, unable
-// to tell these reads from the stage loads still landing in other LDS buffers,
-// would otherwise drain every outstanding vector-memory load first.
+// Eight ds_read_b64_tr_b16, at a[m] and at a[m] + OFF bytes (the same rows of
+// the next block), issued without waiting; tr_wait8 later waits for every LDS
+// read and hands the registers on through the wait, so nothing reads them
+// before the data has landed.  In asm because the compiler, unable to tell
+// these reads from the stage loads still landing in other LDS buffers, would
+// otherwise drain every outstanding vector-memory load first.
 template <int OFF>
-__device__ __forceinline__ void tr_read8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x2_t (&o)[8]) {
+__device__ __forceinline__ void tr_issue8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x2_t (&o)[8]) {
     asm volatile(
         "ds_read_b64_tr_b16 %0, %8\n\t"
         "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
@@ -497,11 +499,16 @@ __device__ __forceinline__ void tr_read8(uint32_t a0, uint32_t a1, uint32_t a2, 
         "ds_read_b64_tr_b16 %4, %10\n\t"
         "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
         "ds_read_b64_tr_b16 %6, %11\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
-        "s_waitcnt lgkmcnt(0)"
+        "ds_read_b64_tr_b16 %7, %11 offset:%12"
         : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
         : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(OFF)
         : "memory");
+}
+__device__ __forceinline__ void tr_wait8(u32x2_t (&o)[8]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]), "+v"(o[6]), "+v"(o[7])
+                 :
+                 : "memory");
 }
 
 // A wave-uniform 32-bit read through the scalar cache.  The compiler would
@@ -650,6 +657,27 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
             for (int k = 0; k < KS; ++k)
                 ka[h][k] = *reinterpret_cast<const QV*>(kt + row * D + ((4 * k + r) ^ chunk_swizzle<D>(row)) * 8);
         }
+        // V^T operand, dims 16 mt + c, tokens 4 r .. +3 of block 0 then of block 1,
+        // read now so that its LDS latency overlaps the K reads' (375 instead of
+        // 382 us on a 16 x (2048 + 512)-token causal chunk workload).
+        // ds_read_b64_tr_b16 builds, in each 16-lane group, row k from the 4
+        // elements lanes 4k .. 4k + 3 point at and hands lane i element i of rows
+        // 0 .. 3; so lane (r, c) points at token 4 r + c / 4, dims 16 mt + 4 (c % 4).
+        // Block 1's rows sit 16 rows (16 * ROWB bytes) after block 0's, with the same swizzle.
+        const int vrow = 4 * r + (c >> 2);
+        const uint32_t vrow_addr =
+            (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)(vt + vrow * D) + (c & 1) * 8;
+        u32x2_t vh[MT / 4][8];
+#pragma unroll
+        for (int m4 = 0; m4 < MT; m4 += 4) {
+            uint32_t a[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int lc = 2 * (m4 + u) + ((c & 3) >> 1);
+                a[u] = vrow_addr + (uint32_t)((lc ^ chunk_swizzle<D>(vrow)) * 16);
+            }
+            tr_issue8<kBlock * ROWB>(a[0], a[1], a[2], a[3], vh[m4 / 4]);
+        }
         const int tok = 2 * j * kBlock + 4 * r;
         QV pb[R];
 #pragma unroll
@@ -690,27 +718,12 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
             l_run[rg] = add_pair<QDT>(pw.w, add_pair<QDT>(pw.z, add_pair<QDT>(pw.y, add_pair<QDT>(pw.x, l_run[rg]))));
             pb[rg] = __builtin_bit_cast(QV, pw);
         }
-        // V^T operand, dims 16 mt + c, tokens 4 r .. +3 of block 0 then of block 1.
-        // ds_read_b64_tr_b16 builds, in each 16-lane group, row k from the 4
-        // elements lanes 4k .. 4k + 3 point at and hands lane i element i of rows
-        // 0 .. 3; so lane (r, c) points at token 4 r + c / 4, dims 16 mt + 4 (c % 4).
-        // Block 1's rows sit 16 rows (16 * ROWB bytes) after block 0's, with the same swizzle.
-        const int vrow = 4 * r + (c >> 2);
-        const uint32_t vrow_addr =
-            (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)(vt + vrow * D) + (c & 1) * 8;
 #pragma unroll
         for (int m4 = 0; m4 < MT; m4 += 4) {
-            uint32_t a[4];
+            tr_wait8(vh[m4 / 4]);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int lc = 2 * (m4 + u) + ((c & 3) >> 1);
-                a[u] = vrow_addr + (uint32_t)((lc ^ chunk_swizzle<D>(vrow)) * 16);
-            }
-            u32x2_t vh[8];
-            tr_read8<kBlock * ROWB>(a[0], a[1], a[2], a[3], vh);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const QV va = __builtin_bit_cast(QV, make_uint4(vh[2 * u].x, vh[2 * u].y, vh[2 * u + 1].x, vh[2 * u + 1].y));
+                const QV va = __builtin_bit_cast(QV, make_uint4(vh[m4 / 4][2 * u].x, vh[m4 / 4][2 * u].y, vh[m4 / 4][2 * u + 1].x, vh[m4 / 4][2 * u + 1].y));
 #pragma unroll
                 for (int rg = 0; rg < R; ++rg) acc[rg][m4 + u] = mma_k32<QDT>(va, pb[rg], acc[rg][m4 + u]);
             }
