@@ -953,6 +953,44 @@ __global__ __launch_bounds__(64) void paged_decode_reduce(DecodeParams p) {
     const int64_t base = ((int64_t)b * p.H_q + hq) * p.max_parts;
     const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + base;
     const float* po = p.ws_o + base * D;
+    const bool live = D >= 64 || lane < D;
+
+    // Up to kFewParts partitions: every partial output is loaded before the
+    // max is known, so those loads overlap the (m, l) load and the two wave
+    // reductions instead of waiting for them.  Same operations in the same
+    // order as the general loop below, so the same bits.
+    constexpr int kFewParts = 16;
+    if (nparts <= kFewParts) {
+        float ov[kFewParts][DPL];
+#pragma unroll
+        for (int t = 0; t < kFewParts; ++t)
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) ov[t][i] = t < nparts && live ? po[(int64_t)t * D + lane + 64 * i] : 0.0f;
+        const float2 v = lane < nparts ? ml[lane] : make_float2(-INFINITY, 0.0f);
+        const float M = wave_max(v.x);
+        float L = 0.0f, o[DPL];
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o[i] = 0.0f;
+        if (M != -INFINITY) {
+            const float w = lane < nparts ? fast_exp2(v.x - M) : 0.0f;
+            if (lane < nparts) L = fmaf(v.y, w, L);
+#pragma unroll
+            for (int t = 0; t < kFewParts; ++t) {
+                if (t < nparts) {
+                    const float wt = lane_bcast(w, t);
+#pragma unroll
+                    for (int i = 0; i < DPL; ++i) o[i] = fmaf(ov[t][i], wt, o[i]);
+                }
+            }
+        }
+        L = wave_sum(L);
+        if (live) {
+#pragma unroll
+            for (int i = 0; i < DPL; ++i)
+                store_out<QDT>(p.out, ((int64_t)b * p.H_q + hq) * D + lane + 64 * i, L > 0.0f ? o[i] / L : 0.0f);
+        }
+        return;
+    }
 
     float M = -INFINITY;
     for (int t0 = 0; t0 < nparts; t0 += 64)
@@ -962,7 +1000,6 @@ __global__ __launch_bounds__(64) void paged_decode_reduce(DecodeParams p) {
     float L = 0.0f, o[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) o[i] = 0.0f;
-    const bool live = D >= 64 || lane < D;
     if (M != -INFINITY) {
         for (int t0 = 0; t0 < nparts; t0 += 64) {
             const int t = t0 + lane;
