@@ -237,7 +237,8 @@ def bench_prefill(args):
     stats = pool.profile_read()
     pool.profile_enable(False)
     pool.close()
-    kern = {k: {"launches": v["launches"], "avg_us": round(v["total_ms"] / max(1, v["launches"]) * 1e3, 3)}
+    kern = {k: {"launches": v["launches"], "timed": v["launches"] - v["dropped"],
+                "avg_us": round(v["total_ms"] / max(1, v["launches"] - v["dropped"]) * 1e3, 3)}
             for k, v in stats.items()}
     flops = w.flops()
     pre_us = kern["paged_prefill"]["avg_us"]
@@ -266,8 +267,8 @@ def bench_prefill(args):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_for(w.name, "paged_prefill", 0), "kernel": "paged_prefill",
                      "algorithmic_flops_per_launch": flops,
-                     "timing": "HIP events around each launch on the library's stream, over a second pass "
-                               "of the same K steps"},
+                     "timing": "a HIP event pair per launch on the library's stream, recorded by the kernel's own "
+                               "start and end (hipExtLaunchKernel), over a second pass of the same K steps"},
         "kernel_hash": kernel_hash("paged_prefill"),
     }
     result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_budget)
@@ -406,9 +407,9 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
-    # Per-kernel durations: the same K steps again, with the library recording an
-    # event pair around every launch.  Those events cost about 10 us of idle
-    # time per kernel boundary, so they stay out of the pass that gives value.
+    # Per-kernel durations: the same K steps again, each kernel recording an
+    # event pair at its own start and end.  Kept out of the pass that gives
+    # value all the same, so that nothing but the steps runs in that region.
     pool.profile_enable(True)
     pool.profile_read()
     torch.cuda.synchronize()
@@ -422,7 +423,8 @@ def main():
         ", ".join(f"{m} {d['p10']}/{d['p50']}/{d['p90']}" for m, d in step_dist.items()))
 
     kv_bytes = w.kv_bytes_per_step()
-    kern = {k: {"launches": v["launches"], "avg_us": round(v["total_ms"] / max(1, v["launches"]) * 1e3, 3)}
+    kern = {k: {"launches": v["launches"], "timed": v["launches"] - v["dropped"],
+                "avg_us": round(v["total_ms"] / max(1, v["launches"] - v["dropped"]) * 1e3, 3)}
             for k, v in stats.items()}
     part_us = kern.get("paged_decode_partition", {}).get("avg_us")
     red_us = kern.get("paged_decode_reduce", {}).get("avg_us", 0.0)
@@ -458,8 +460,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
                      "traffic": traffic, "kernel": "paged_decode_partition",
                      "algorithmic_bytes_per_launch": kv_bytes,
-                     "timing": "HIP events around each launch on the library's stream, over a second pass "
-                               "of the same K steps"},
+                     "timing": "a HIP event pair per launch on the library's stream, recorded by the kernel's own "
+                               "start and end (hipExtLaunchKernel), over a second pass of the same K steps"},
         "kernel_hash": kernel_hash(),
     }
     pool.close()

@@ -415,12 +415,15 @@ int kv_pool_copy_to_host(const kv_pool_t* pool, void* k_dst, void* v_dst);
  * Measurement
  * ------------------------------------------------------------------------ */
 
-/* Per-kernel timing: while enabled, every kernel the pool launches is
- * bracketed by HIP events on its launch stream.  pkv_profile_read waits for
+/* Per-kernel timing: while enabled, each call's kernels record a HIP event
+ * pair on their launch stream as they start and end (hipExtLaunchKernel; the
+ * pair spans a call's first kernel to its last).  pkv_profile_read waits for
  * the recorded events, fills up to cap entries of `out` with the launches
  * and summed device milliseconds per kernel name since the last read, and
  * resets the counters.  At most 65536 launches per kernel are kept between
- * reads; more are counted in `dropped`. */
+ * reads; launches not timed (beyond that, or when an event is missing) are
+ * counted in `dropped` and are not in total_ms, so the mean duration is
+ * total_ms / (launches - dropped). */
 typedef struct {
     char name[48];
     int64_t launches;

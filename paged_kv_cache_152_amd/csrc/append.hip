@@ -267,7 +267,7 @@ hipError_t launch_move_blocks(const MoveParams& p, hipStream_t stream) {
     MoveParams arg = p;
     void* args[] = {&arg};
     const int64_t threads = 2 * (p.block_bytes / 16);
-    return hipLaunchKernel(reinterpret_cast<const void*>(kv_move_blocks),
+    return launch_kernel(reinterpret_cast<const void*>(kv_move_blocks),
                            dim3((unsigned)((threads + 255) / 256), (unsigned)p.n), dim3(256), args, 0, stream);
 }
 
@@ -276,7 +276,7 @@ hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream) {
     CopyParams arg = p;
     void* args[] = {&arg};
     const int64_t threads = 2 * (p.block_bytes / 16);
-    return hipLaunchKernel(reinterpret_cast<const void*>(kv_copy_blocks),
+    return launch_kernel(reinterpret_cast<const void*>(kv_copy_blocks),
                            dim3((unsigned)((threads + 255) / 256), (unsigned)p.n), dim3(256), args, 0, stream);
 }
 
@@ -286,20 +286,20 @@ hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream) {
     if (p.dst_dt == DT_INT8) {
         if (!p.tags || p.epoch == 0) return hipErrorInvalidValue;
         void* args[] = {&arg};
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kv_append_int8_tag),
+        hipError_t e = launch_kernel(reinterpret_cast<const void*>(kv_append_int8_tag),
                                        dim3((unsigned)((p.T + 255) / 256)), dim3(256), args, 0, stream);
         if (e != hipSuccess) return e;
         const void* fn = p.src_dt == DT_F32   ? reinterpret_cast<const void*>(kv_append_int8<DT_F32>)
                          : p.src_dt == DT_F16 ? reinterpret_cast<const void*>(kv_append_int8<DT_F16>)
                                               : reinterpret_cast<const void*>(kv_append_int8<DT_BF16>);
-        return hipLaunchKernel(fn, dim3((unsigned)p.T, (unsigned)p.H_kv), dim3(64), args, 0, stream);
+        return launch_kernel(fn, dim3((unsigned)p.T, (unsigned)p.H_kv), dim3(64), args, 0, stream);
     }
     if (p.dst_dt == p.src_dt) {
         int row_bytes = p.D * elem_bytes(p.dst_dt);
         const int64_t threads = 2LL * p.T * p.H_kv * (row_bytes / 16);
         const unsigned blocks = (unsigned)((threads + 255) / 256);
         void* args[] = {&arg, &row_bytes};
-        return hipLaunchKernel(reinterpret_cast<const void*>(kv_append_copy), dim3(blocks), dim3(256), args,
+        return launch_kernel(reinterpret_cast<const void*>(kv_append_copy), dim3(blocks), dim3(256), args,
                                0, stream);
     }
     if (p.dst_dt == DT_FP8 && (p.src_dt == DT_BF16 || p.src_dt == DT_F32)) {
@@ -308,7 +308,7 @@ hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream) {
         void* args[] = {&arg};
         const void* fn = p.src_dt == DT_BF16 ? reinterpret_cast<const void*>(kv_append_fp8<DT_BF16>)
                                              : reinterpret_cast<const void*>(kv_append_fp8<DT_F32>);
-        return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, stream);
+        return launch_kernel(fn, dim3(blocks), dim3(256), args, 0, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -321,7 +321,7 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t str
     uint4* d = reinterpret_cast<uint4*>(dst);
     const uint4* s = reinterpret_cast<const uint4*>(src);
     void* args[] = {&d, &s, &n};
-    return hipLaunchKernel(reinterpret_cast<const void*>(pkv_copy_kernel), dim3((unsigned)blocks), dim3(256),
+    return launch_kernel(reinterpret_cast<const void*>(pkv_copy_kernel), dim3((unsigned)blocks), dim3(256),
                            args, 0, stream);
 }
 

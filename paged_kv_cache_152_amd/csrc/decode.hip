@@ -1166,7 +1166,7 @@ int decode_resident_workgroups(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream) {
     DecodeParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(paged_decode_plan), dim3(1), dim3(kPlanThreads), args, 0,
+    return launch_kernel(reinterpret_cast<const void*>(paged_decode_plan), dim3(1), dim3(kPlanThreads), args, 0,
                            stream);
 }
 
@@ -1182,7 +1182,7 @@ hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream) {
     }
     DecodeParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, dim3(kDecodeWaves * 64), args, 0, stream);
+    return launch_kernel(reinterpret_cast<const void*>(fn), grid, dim3(kDecodeWaves * 64), args, 0, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {
@@ -1190,7 +1190,7 @@ hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {
     if (!fn) return hipErrorInvalidValue;
     DecodeParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)p.H_q, (unsigned)p.B),
+    return launch_kernel(reinterpret_cast<const void*>(fn), dim3((unsigned)p.H_q, (unsigned)p.B),
                            dim3(64), args, 0, stream);
 }
 

@@ -107,6 +107,17 @@ struct PrefillParams {
     float scale;
 };
 
+// Every kernel of the library is launched through launch_kernel (same
+// arguments as hipLaunchKernel).  While a timed call has armed an event pair,
+// the launches go through hipExtLaunchKernel: the first records the start
+// event as its kernel starts and every one records the stop event as its
+// kernel ends, so the pair spans exactly the call's kernels.  Two separate
+// hipEventRecord calls around the launch would also count the dispatch and
+// completion of the event packets themselves (about 5 us a launch).
+hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, size_t shmem, hipStream_t stream);
+void arm_launch_events(hipEvent_t start, hipEvent_t stop);
+bool disarm_launch_events();   // true if a launch since arming recorded the events
+
 // Launch one kernel each; return hipSuccess or the launch error.
 // Unsupported combinations are filtered on the host before these are called.
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);

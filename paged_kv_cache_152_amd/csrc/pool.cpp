@@ -8,6 +8,7 @@
 // per-block reference count so several tables can share prefix blocks.  A
 // block whose count drops to zero goes to the back of the free list.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cmath>
@@ -251,7 +252,8 @@ KernelTimer& timer_for(kv_pool* p, const char* name) {
     return p->timers.back();
 }
 
-// Launch `fn` on `stream`, bracketed by events when profiling.
+// Launch `fn` on `stream`; when profiling, the kernels it launches record an
+// event pair at their own start and end (launch_kernel).
 template <class F>
 hipError_t timed_launch(kv_pool* p, const char* name, hipStream_t stream, F&& fn) {
     if (!p->profiling) return fn();
@@ -268,14 +270,9 @@ hipError_t timed_launch(kv_pool* p, const char* name, hipStream_t stream, F&& fn
         if (b) p->spare_events.push_back(b);
         return fn();
     }
-    if (hipEventRecord(a, stream) != hipSuccess) {   // no timing for this launch
-        ++t.dropped;
-        p->spare_events.push_back(a);
-        p->spare_events.push_back(b);
-        return fn();
-    }
-    hipError_t e = fn();
-    if (hipEventRecord(b, stream) != hipSuccess) {
+    pkv::arm_launch_events(a, b);              // the launches inside fn record them
+    const hipError_t e = fn();
+    if (!pkv::disarm_launch_events()) {        // nothing launched: no timing for this call
         ++t.dropped;
         p->spare_events.push_back(a);
         p->spare_events.push_back(b);
@@ -1175,3 +1172,33 @@ int pkv_copy(void* dst, const void* src, size_t bytes, void* stream) {
 }
 
 }  // extern "C"
+
+namespace pkv {
+namespace {
+// The event pair a timed call armed on this thread, and whether a launch has
+// recorded it yet.
+thread_local hipEvent_t t_start = nullptr, t_stop = nullptr;
+thread_local bool t_recorded = false;
+}  // namespace
+
+void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
+    t_start = start;
+    t_stop = stop;
+    t_recorded = false;
+}
+
+bool disarm_launch_events() {
+    const bool r = t_recorded;
+    t_start = t_stop = nullptr;
+    t_recorded = false;
+    return r;
+}
+
+hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, size_t shmem, hipStream_t stream) {
+    if (!t_stop) return hipLaunchKernel(fn, grid, block, args, shmem, stream);
+    const hipError_t e =
+        hipExtLaunchKernel(fn, grid, block, args, shmem, stream, t_recorded ? nullptr : t_start, t_stop, 0);
+    if (e == hipSuccess) t_recorded = true;
+    return e;
+}
+}  // namespace pkv

@@ -825,7 +825,7 @@ hipError_t launch_prefill(const PrefillParams& p, int32_t max_q_len, hipStream_t
     PrefillParams arg = p;
     arg.tiles = prefill_tiles(p.G, max_q_len);
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n_wg), dim3(kPfWaves * 64), args, 0,
+    return launch_kernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n_wg), dim3(kPfWaves * 64), args, 0,
                            stream);
 }
 
