@@ -317,6 +317,35 @@ def test_deterministic():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("dt,Hq,Hkv", [(wl.F16, 8, 8), (wl.BF16, 32, 8), (wl.F16, 40, 8), (wl.E4M3, 32, 8)])
+def test_decode_bit_identical_across_runs(dt, Hq, Hkv):
+    """Twelve launches of one decode give the same bits, on the vector kernel
+    (MHA) and the matrix-core kernel (groups 4 and 5, FP8): the work list
+    decides which workgroup computes an item, never the item's arithmetic or
+    the order of the merge."""
+    w = _small(dt, Hq, Hkv, 128, [3000, 1, 2049, 700, 4100, 16, 9000, 257], seed=71 + Hq)
+    prep = harness.prepare(w, partition_tokens=256)
+    prep.append_step()
+    outs = [harness.out_to_f64(prep.decode()) for _ in range(12)]
+    prep.pool.close()
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"run {i} differs in {int((outs[0] != o).sum())} elements"
+    assert_close(outs[0], expected(w), dt, "deterministic")
+
+
+@pytest.mark.parametrize("name", ["gqa8b", "fp8"])
+def test_full_size_decode_bit_identical_across_runs(name):
+    """Five launches at full size (768 resident workgroups taking items from
+    the work list under full HBM load) give the same bits."""
+    w = wl.make(name)
+    prep = harness.prepare(w)
+    prep.append_step()
+    outs = [harness.out_to_f64(prep.decode()) for _ in range(5)]
+    prep.pool.close()
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"{name}: run {i} differs in {int((outs[0] != o).sum())} elements"
+
+
 def test_zero_lengths_and_bad_table_entries():
     w = _small(wl.F16, 8, 2, 128, [100, 40], seed=41)
     prep = harness.prepare(w, partition_tokens=64)
