@@ -915,7 +915,8 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
 }
 
 template <int KDT, int QDT, int GS>
-__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+// Groups up to 5 fit 3 waves per SIMD without spilling; larger ones take 2.
+__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(GS <= 5 ? 3 : 2)))
 void paged_decode_partition_gqa(DecodeParams p) {
     __shared__ StreamSmem<kDecodeWaves * 4, GS, 128> sm;
     for_each_item(p, [&](int b, int part, int hgi, int P) { gqa_item<KDT, QDT, GS>(p, b, part, hgi, P, sm); });
