@@ -245,13 +245,16 @@ def test_uniform_lengths_automatic_partition(dt):
     assert_close(fixed, want, dt, "fixed 1024")
 
 
-@pytest.mark.parametrize("dt", [wl.BF16, wl.F16, wl.E4M3])
+@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("dt", [wl.F32, wl.BF16, wl.F16, wl.E4M3])
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16])
-def test_every_group_size(dt, G):
+def test_every_group_size(dt, G, D):
     """Every query-head group size the kernels instantiate (1 to 8 heads per
-    workgroup; 12 and 16 split into groups of 6 and 8) against the oracle,
-    over one-partition and multi-partition contexts."""
-    w = _small(dt, 2 * G, 2, 128, [700, 1, 129, 2100], seed=90 + G)
+    workgroup; 12 and 16 split into groups of 6 and 8), on the vector kernel
+    (all dtypes at head_dim 16 and 64, fp32 and groups 1-2 at 128) and the
+    matrix-core kernel (16-bit and FP8 at 128, groups 3 and up), against the
+    oracle over one-partition and multi-partition contexts."""
+    w = _small(dt, 2 * G, 2, D, [700, 1, 129, 2100], seed=90 + G + D)
     for P in (256, 0):
         got = run_case(w, partition=P)
         assert_close(got, expected(w), dt, f"G={G} P={P}")
