@@ -112,8 +112,11 @@ SHAPES = [(37, 37), (300, 45), (129, 1), (64, 16), (17, 3)]
 
 @pytest.mark.parametrize("kv_dt", [wl.F16, wl.BF16, wl.E4M3])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G", [1, 4, 5, 8])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8, 11, 16, 24, 32])
 def test_prefill_vs_oracle(kv_dt, D, G):
+    """Every row-group shape: G <= 16 query heads share one row group (32 / G
+    tokens per wave, padding rows when G does not divide 32); 24 and 32 split
+    into two groups of 12 and of 16."""
     H_kv = 2
     c = Case(kv_dt, G * H_kv, H_kv, D, SHAPES, seed=1000 + 10 * G + D + kv_dt)
     for causal in (True, False):
