@@ -134,7 +134,8 @@ def test_int8_append_codes_bit_exact(src_dt, D):
 
 
 @pytest.mark.parametrize("q_dt", [wl.BF16, wl.F16])
-@pytest.mark.parametrize("D,G", [(128, 1), (128, 2), (128, 4), (128, 8), (64, 1), (64, 5), (16, 3)])
+@pytest.mark.parametrize("D,G", [(128, 1), (128, 2), (128, 3), (128, 4), (128, 5), (128, 6), (128, 7), (128, 8),
+                                 (64, 1), (64, 5), (64, 8), (16, 3), (16, 8)])
 def test_int8_decode_vs_oracle(q_dt, D, G):
     H_kv = 2
     c = Int8Case(H_kv, D, [1, 37, 130, 300, 16, 0], wl.BF16, seed=200 + D + G + q_dt)
