@@ -504,6 +504,21 @@ __device__ __forceinline__ void tr_issue8(uint32_t a0, uint32_t a1, uint32_t a2,
         : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(OFF)
         : "memory");
 }
+// Eight ds_read_b64_tr_b8 at a[0..7], issued without waiting (tr_wait8 waits).
+__device__ __forceinline__ void trb8_issue8(const uint32_t (&a)[8], u32x2_t (&o)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %8\n\t"
+        "ds_read_b64_tr_b8 %1, %9\n\t"
+        "ds_read_b64_tr_b8 %2, %10\n\t"
+        "ds_read_b64_tr_b8 %3, %11\n\t"
+        "ds_read_b64_tr_b8 %4, %12\n\t"
+        "ds_read_b64_tr_b8 %5, %13\n\t"
+        "ds_read_b64_tr_b8 %6, %14\n\t"
+        "ds_read_b64_tr_b8 %7, %15"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
 __device__ __forceinline__ void tr_wait8(u32x2_t (&o)[8]) {
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]), "+v"(o[6]), "+v"(o[7])
@@ -520,23 +535,27 @@ __device__ __forceinline__ int32_t scalar_read(const int32_t* ptr) {
     return v;
 }
 
-template <int KDT, int D>
+template <int KDT, int QDT, int D>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill_dma_kernel(PrefillParams p) {
-    constexpr int QDT = KDT;
+    constexpr bool F8 = KDT == DT_FP8;         // E4M3 codes: widened as they leave LDS
+    constexpr int PT = F8 ? DT_F16 : KDT;      // type of P and V in P.V
     constexpr int KS = D / 32;                 // S^T steps per block (32 dims each)
     constexpr int MT = D / 16;                 // O^T m-tiles (16 dims each)
     constexpr int R = kRowGroups;
-    constexpr int ROWB = D * 2;                // bytes of a token row
+    constexpr int ROWB = D * (F8 ? 1 : 2);     // bytes of a token row
+    constexpr int SWZ = ROWB / 2;              // chunk_swizzle<SWZ>: the swizzle of a row of ROWB bytes
     constexpr int CH = ROWB / 16;              // 16-byte chunks per row
     constexpr int SROWS = 2 * kBlock;          // token rows per stage
     constexpr int NI = SROWS * CH / (64 * kPfWaves);   // loads per wave per tensor per stage
-    constexpr int SE = SROWS * D;              // 16-bit elements of one tensor's stage
+    constexpr int SB = SROWS * ROWB;           // bytes of one tensor's stage
     constexpr float kLazy = 8.0f;
     static_assert(NI >= 1 && (64 / CH) * NI * kPfWaves == SROWS, "stage rows split evenly over the loads");
+    static_assert(F8 ? QDT != KDT : QDT == KDT, "16-bit pools take queries of their own type");
     using QV = typename Vec8<QDT>::T;
+    using PV = typename Vec8<PT>::T;
     typedef __attribute__((address_space(3))) void lds_void;
-    __shared__ __align__(16) uint16_t k_lds[kStages][SE];
-    __shared__ __align__(16) uint16_t v_lds[kStages][SE];
+    __shared__ __align__(16) unsigned char k_lds[kStages][SB];
+    __shared__ __align__(16) unsigned char v_lds[kStages][SB];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane >> 4, c = lane & 15;
@@ -564,7 +583,12 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
 
     // A negative scale flips q's sign bits (exact) so that the logit scale is
     // positive and the row max can be taken before scaling.
-    const float scale2 = p.scale * kLog2e;
+    float scale2 = p.scale * kLog2e;
+    float vscale = 1.0f;
+    if constexpr (F8) {                        // FP8: the K scale joins the logit scale, the V scale the output
+        scale2 *= p.k_scale[g];
+        vscale = p.v_scale[g];
+    }
     const uint32_t qflip = scale2 < 0.0f ? 0x80008000u : 0u;
     const float qscale = fmaxf(fabsf(scale2), 1e-30f);
 
@@ -603,7 +627,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         const int slot = (wave * NI + i) * 64 + lane;
         const int row = slot / CH, pch = slot % CH;
         ld_row[i] = row;
-        ld_off[i] = (row % kBlock) * ROWB + ((pch ^ chunk_swizzle<D>(row)) * 16);
+        ld_off[i] = (row % kBlock) * ROWB + ((pch ^ chunk_swizzle<SWZ>(row)) * 16);
     }
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto issue = [&](int jj) {                 // the loads of stage jj (blocks 2 jj, 2 jj + 1)
@@ -618,7 +642,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         for (int i = 0; i < NI; ++i) {
             const int h = ((wave_u * NI + i) * (64 / CH)) / kBlock;          // uniform: block of this load
             const int ph = h ? ph1 : ph0;
-            const int dst = (wave_u * NI + i) * 64 * 8;                       // 16-bit elements
+            const int dst = (wave_u * NI + i) * 64 * 16;                      // bytes
             const char* ks;
             const char* vs;
             if (full) {                        // uniform base + 32-bit lane offset
@@ -646,16 +670,22 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
 
     const int wg_min_see = p.causal ? n - q_len + tile0 : n - 1;
     auto compute = [&](bool masked, int j, int buf) {
-        const uint16_t* kt = k_lds[buf];
-        const uint16_t* vt = v_lds[buf];
-        // K operand of block h: token c, dims 32 k + 8 r .. +7
+        const unsigned char* kt = k_lds[buf];
+        const unsigned char* vt = v_lds[buf];
+        // K operand of block h: token c, dims 32 k + 8 r .. +7 (16 bytes, or 8
+        // E4M3 codes widened exactly to q's type)
         QV ka[2][KS];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int row = h * kBlock + c;
 #pragma unroll
-            for (int k = 0; k < KS; ++k)
-                ka[h][k] = *reinterpret_cast<const QV*>(kt + row * D + ((4 * k + r) ^ chunk_swizzle<D>(row)) * 8);
+            for (int k = 0; k < KS; ++k) {
+                if constexpr (F8)
+                    ka[h][k] = __builtin_bit_cast(QV, fp8x8_to<QDT>(*reinterpret_cast<const uint2*>(
+                        kt + row * ROWB + ((2 * k + (r >> 1)) ^ chunk_swizzle<SWZ>(row)) * 16 + (r & 1) * 8)));
+                else
+                    ka[h][k] = *reinterpret_cast<const QV*>(kt + row * ROWB + ((4 * k + r) ^ chunk_swizzle<SWZ>(row)) * 16);
+            }
         }
         // V^T operand, dims 16 mt + c, tokens 4 r .. +3 of block 0 then of block 1,
         // read now so that its LDS latency overlaps the K reads' (375 instead of
@@ -664,22 +694,44 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         // elements lanes 4k .. 4k + 3 point at and hands lane i element i of rows
         // 0 .. 3; so lane (r, c) points at token 4 r + c / 4, dims 16 mt + 4 (c % 4).
         // Block 1's rows sit 16 rows (16 * ROWB bytes) after block 0's, with the same swizzle.
-        const int vrow = 4 * r + (c >> 2);
-        const uint32_t vrow_addr =
-            (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)(vt + vrow * D) + (c & 1) * 8;
-        u32x2_t vh[MT / 4][8];
+        // E4M3 pools: ds_read_b64_tr_b8 builds, in each 16-lane group, row k
+        // from the 16 bytes lanes 2k, 2k + 1 point at and hands lane i byte i
+        // of rows 0 .. 7.  Lane (r, c) points at the token that k-index
+        // 8 r + c / 2 stands for (tokens 4 r .. +3 of block 0, then of block
+        // 1), dims 16 mt + 8 (c % 2) .. +7, so one read per m-tile gives the
+        // lane its 8 codes of dim 16 mt + c, widened exactly to f16.
+        constexpr int NV = F8 ? MT / 8 : MT / 4;          // issue groups of 8 reads
+        u32x2_t vh[NV][8];
+        if constexpr (F8) {
+            const int kk = c >> 1;
+            const int trow = kk < 4 ? 4 * r + kk : kBlock + 4 * r + (kk - 4);
+            const uint32_t rbase =
+                (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(vt + trow * ROWB) + (c & 1) * 8;
+            const int sw = chunk_swizzle<SWZ>(trow);
 #pragma unroll
-        for (int m4 = 0; m4 < MT; m4 += 4) {
-            uint32_t a[4];
+            for (int m8 = 0; m8 < MT; m8 += 8) {
+                uint32_t a8[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int lc = 2 * (m4 + u) + ((c & 3) >> 1);
-                a[u] = vrow_addr + (uint32_t)((lc ^ chunk_swizzle<D>(vrow)) * 16);
+                for (int u = 0; u < 8; ++u) a8[u] = rbase + (uint32_t)(((m8 + u) ^ sw) * 16);
+                trb8_issue8(a8, vh[m8 / 8]);
             }
-            tr_issue8<kBlock * ROWB>(a[0], a[1], a[2], a[3], vh[m4 / 4]);
+        } else {
+            const int vrow = 4 * r + (c >> 2);
+            const uint32_t vrow_addr =
+                (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(vt + vrow * ROWB) + (c & 1) * 8;
+#pragma unroll
+            for (int m4 = 0; m4 < MT; m4 += 4) {
+                uint32_t a[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int lc = 2 * (m4 + u) + ((c & 3) >> 1);
+                    a[u] = vrow_addr + (uint32_t)((lc ^ chunk_swizzle<SWZ>(vrow)) * 16);
+                }
+                tr_issue8<kBlock * ROWB>(a[0], a[1], a[2], a[3], vh[m4 / 4]);
+            }
         }
         const int tok = 2 * j * kBlock + 4 * r;
-        QV pb[R];
+        PV pb[R];
 #pragma unroll
         for (int rg = 0; rg < R; ++rg) {
             f32x4_t S0 = {0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
@@ -713,19 +765,32 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
             // l sums the rounded weights P.V multiplies (a normalised average of
             // them); each lane keeps the part of its own tokens, all four lanes of
             // a row rescale alike, and the parts are added at the end
-            const uint4 pw = make_uint4(pack2<QDT>(pr[0], pr[1]), pack2<QDT>(pr[2], pr[3]),
-                                        pack2<QDT>(pr[4], pr[5]), pack2<QDT>(pr[6], pr[7]));
-            l_run[rg] = add_pair<QDT>(pw.w, add_pair<QDT>(pw.z, add_pair<QDT>(pw.y, add_pair<QDT>(pw.x, l_run[rg]))));
-            pb[rg] = __builtin_bit_cast(QV, pw);
+            const uint4 pw = make_uint4(pack2<PT>(pr[0], pr[1]), pack2<PT>(pr[2], pr[3]),
+                                        pack2<PT>(pr[4], pr[5]), pack2<PT>(pr[6], pr[7]));
+            l_run[rg] = add_pair<PT>(pw.w, add_pair<PT>(pw.z, add_pair<PT>(pw.y, add_pair<PT>(pw.x, l_run[rg]))));
+            pb[rg] = __builtin_bit_cast(PV, pw);
         }
+        if constexpr (F8) {
 #pragma unroll
-        for (int m4 = 0; m4 < MT; m4 += 4) {
-            tr_wait8(vh[m4 / 4]);
+            for (int m8 = 0; m8 < MT; m8 += 8) {
+                tr_wait8(vh[m8 / 8]);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const QV va = __builtin_bit_cast(QV, make_uint4(vh[m4 / 4][2 * u].x, vh[m4 / 4][2 * u].y, vh[m4 / 4][2 * u + 1].x, vh[m4 / 4][2 * u + 1].y));
+                for (int u = 0; u < 8; ++u) {
+                    const PV va = __builtin_bit_cast(PV, fp8x8_to<DT_F16>(make_uint2(vh[m8 / 8][u].x, vh[m8 / 8][u].y)));
 #pragma unroll
-                for (int rg = 0; rg < R; ++rg) acc[rg][m4 + u] = mma_k32<QDT>(va, pb[rg], acc[rg][m4 + u]);
+                    for (int rg = 0; rg < R; ++rg) acc[rg][m8 + u] = mma_k32<PT>(va, pb[rg], acc[rg][m8 + u]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m4 = 0; m4 < MT; m4 += 4) {
+                tr_wait8(vh[m4 / 4]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const PV va = __builtin_bit_cast(PV, make_uint4(vh[m4 / 4][2 * u].x, vh[m4 / 4][2 * u].y, vh[m4 / 4][2 * u + 1].x, vh[m4 / 4][2 * u + 1].y));
+#pragma unroll
+                    for (int rg = 0; rg < R; ++rg) acc[rg][m4 + u] = mma_k32<PT>(va, pb[rg], acc[rg][m4 + u]);
+                }
             }
         }
     };
@@ -755,7 +820,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     for (int rg = 0; rg < R; ++rg) {
         if (!live[rg]) continue;
         const int row = rg * 16 + c;
-        const float inv = l_run[rg] > 0.0f ? 1.0f / l_run[rg] : 0.0f;
+        const float inv = l_run[rg] > 0.0f ? vscale / l_run[rg] : 0.0f;
         const int64_t orow = ((int64_t)(q0 + i_row[rg]) * p.H_q + hq0 + row % gs) * D;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -782,17 +847,26 @@ KernelFn pick_d(int D) {
 template <int KDT>
 KernelFn pick_dma(int D) {
     switch (D) {
-        case 64: return paged_prefill_dma_kernel<KDT, 64>;
-        case 128: return paged_prefill_dma_kernel<KDT, 128>;
+        case 64: return paged_prefill_dma_kernel<KDT, KDT, 64>;
+        case 128: return paged_prefill_dma_kernel<KDT, KDT, 128>;
         default: return nullptr;
     }
+}
+
+// E4M3 pools: the direct-to-LDS kernel at head_dim 128 (a stage of 64-dim
+// codes is too small for every lane to move 16 bytes), the register-staged
+// kernel at 64.
+template <int QDT>
+KernelFn pick_fp8(int D) {
+    if (D == 128) return paged_prefill_dma_kernel<DT_FP8, QDT, 128>;
+    return pick_d<DT_FP8, QDT>(D);
 }
 
 KernelFn pick(int kdt, int qdt, int D) {
     if (kdt == DT_F16 && qdt == DT_F16) return pick_dma<DT_F16>(D);
     if (kdt == DT_BF16 && qdt == DT_BF16) return pick_dma<DT_BF16>(D);
-    if (kdt == DT_FP8 && qdt == DT_BF16) return pick_d<DT_FP8, DT_BF16>(D);
-    if (kdt == DT_FP8 && qdt == DT_F16) return pick_d<DT_FP8, DT_F16>(D);
+    if (kdt == DT_FP8 && qdt == DT_BF16) return pick_fp8<DT_BF16>(D);
+    if (kdt == DT_FP8 && qdt == DT_F16) return pick_fp8<DT_F16>(D);
     return nullptr;
 }
 
