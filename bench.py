@@ -194,21 +194,24 @@ def bench_prefill(args):
     pool = pkv.KVPool(w.num_blocks, w.H_kv, w.D, w.kv_dtype, free_order=order)
     if args.partition:
         pool.set_partition(args.partition)
+    scales = w.fp8_scales()
+    if scales is not None:
+        pool.set_fp8_scales(*scales)
     seqs, cs, kc, vc = [], [], [], []
     for bi in range(w.B):
         K, V = w.kv(bi)
         s = pool.seq_create()
         seqs.append(s)
         slots = pool.seq_reserve(s, w.n)
-        pool.append(torch.from_numpy(slots[: w.cached]).cuda(), harness.to_device(K[: w.cached], w.kv_dtype),
-                    harness.to_device(V[: w.cached], w.kv_dtype))
+        pool.append(torch.from_numpy(slots[: w.cached]).cuda(), harness.to_device(K[: w.cached], w.src_dtype),
+                    harness.to_device(V[: w.cached], w.src_dtype))
         cs.append(slots[w.cached:])
         kc.append(K[w.cached:])
         vc.append(V[w.cached:])
     slots_d = torch.from_numpy(np.concatenate(cs)).cuda()
-    k_d = harness.to_device(np.concatenate(kc), w.kv_dtype)
-    v_d = harness.to_device(np.concatenate(vc), w.kv_dtype)
-    q = harness.to_device(w.q(), w.kv_dtype)
+    k_d = harness.to_device(np.concatenate(kc), w.src_dtype)
+    v_d = harness.to_device(np.concatenate(vc), w.src_dtype)
+    q = harness.to_device(w.q(), w.src_dtype)
     out = torch.empty_like(q)
     q_start = torch.arange(0, (w.B + 1) * w.chunk, w.chunk, dtype=torch.int32, device="cuda")
     tables, lens = pool.block_tables(seqs, -(-w.n // wl.BLOCK))
@@ -279,11 +282,16 @@ def cpu_baseline_prefill(w, budget_s: float = 15.0):
     """The fp64 oracle's prefill attention on a bounded sample: the last 64 query
     rows of a chunk, per sequence, over 2 sequences per call."""
     import oracle
+    from tests.oracle_ref import fp8_codes
     rows, group = 64, 2
     Ks, Vs, qs = [], [], []
     qall = w.q()
+    scales = w.fp8_scales()
+    kw = dict(k_scale=scales[0], v_scale=scales[1]) if scales is not None else {}
     for bi in range(group):
         K, V = w.kv(bi)
+        if scales is not None:                 # the codes the pool holds
+            K, V = fp8_codes(K, scales[0]), fp8_codes(V, scales[1])
         Ks.append(K)
         Vs.append(V)
         qs.append(qall[(bi + 1) * w.chunk - rows:(bi + 1) * w.chunk])
@@ -296,7 +304,7 @@ def cpu_baseline_prefill(w, budget_s: float = 15.0):
     done, calls = 0.0, 0
     while done < budget_s:
         t0 = time.perf_counter()
-        oracle.prefill_attention(q, w.kv_dtype, q_start, K, V, w.kv_dtype, off, lens, w.scale, causal=w.causal)
+        oracle.prefill_attention(q, w.src_dtype, q_start, K, V, w.kv_dtype, off, lens, w.scale, causal=w.causal, **kw)
         done += time.perf_counter() - t0
         calls += 1
     return {"value": round(calls * flops_call / done / 1e12, 6), "unit": "TFLOP/s",
@@ -357,7 +365,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first; the FP8 and INT8 workloads need about 40 and 90 to reach steady state")
-    ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8", "int8", "prefill8b", "swap"])
+    ap.add_argument("--workload", default="mha7b", choices=["tiny", "mha7b", "gqa8b", "mixed", "fp8", "int8", "prefill8b", "prefill8b_fp8", "swap"])
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)

@@ -374,6 +374,25 @@ class PrefillWorkload:
         return self.cached + self.chunk
 
     @property
+    def src_dtype(self) -> int:
+        """Storage of the generated K/V and of q: bf16 for an FP8 pool (the codes
+        are made by kv_append), else the pool's own type."""
+        return BF16 if self.kv_dtype == E4M3 else self.kv_dtype
+
+    def fp8_scales(self):
+        """Per-kv-head static scales absmax/448 over all generated K (resp. V);
+        None unless the pool is FP8."""
+        if self.kv_dtype != E4M3:
+            return None
+        kmax = np.zeros(self.H_kv, np.float32)
+        vmax = np.zeros(self.H_kv, np.float32)
+        for b in range(self.B):
+            K, V = self.kv(b)
+            kmax = np.maximum(kmax, np.abs(bf16_bits_to_f32(K)).max(axis=(0, 2)))
+            vmax = np.maximum(vmax, np.abs(bf16_bits_to_f32(V)).max(axis=(0, 2)))
+        return (kmax / np.float32(448.0)).astype(np.float32), (vmax / np.float32(448.0)).astype(np.float32)
+
+    @property
     def scale(self) -> float:
         return float(np.float32(1.0 / math.sqrt(self.D)))
 
@@ -385,21 +404,21 @@ class PrefillWorkload:
         return np.random.SeedSequence(self.seed).spawn(self.B + 1)
 
     def kv(self, b: int):
-        """K_b, V_b: [n][H_kv][D] in the pool's storage dtype (bf16 bits, f16)."""
+        """K_b, V_b: [n][H_kv][D] in the source storage dtype (bf16 bits, f16)."""
         import torch
         g = _torch_gen(self._children()[b])
         per = self.n * self.H_kv * self.D
         x = torch.randn(2 * per, generator=g, dtype=torch.float32)
         K = x[:per].reshape(self.n, self.H_kv, self.D)
         V = x[per:].reshape(self.n, self.H_kv, self.D)
-        return cast_to_storage(K, self.kv_dtype), cast_to_storage(V, self.kv_dtype)
+        return cast_to_storage(K, self.src_dtype), cast_to_storage(V, self.src_dtype)
 
     def q(self) -> np.ndarray:
         """[B * chunk][H_q][D], sequence b owning rows b*chunk .. (b+1)*chunk - 1."""
         import torch
         x = torch.randn(self.B * self.chunk * self.H_q * self.D, generator=_torch_gen(self._children()[self.B]),
                         dtype=torch.float32)
-        return cast_to_storage(x.reshape(self.B * self.chunk, self.H_q, self.D), self.kv_dtype)
+        return cast_to_storage(x.reshape(self.B * self.chunk, self.H_q, self.D), self.src_dtype)
 
     def flops(self) -> int:
         """Algorithmic flops of one launch: 2 D for q.k and 2 D for p.v per (query
@@ -417,7 +436,10 @@ class PrefillWorkload:
 
 def make_prefill(name: str) -> PrefillWorkload:
     """prefill8b: Llama-3-8B heads (32 q / 8 kv, d 128), bf16, 16 sequences of
-    2048 cached tokens plus a 512-token chunk, causal."""
+    2048 cached tokens plus a 512-token chunk, causal.  prefill8b_fp8: the same
+    values appended into an FP8-E4M3 pool (per-head scales absmax / 448), q bf16."""
     if name == "prefill8b":
         return PrefillWorkload(name, 6, 16, 32, 8, 128, BF16, 2048, 512)
+    if name == "prefill8b_fp8":
+        return PrefillWorkload(name, 6, 16, 32, 8, 128, E4M3, 2048, 512)
     raise ValueError(f"unknown prefill workload {name!r}")
