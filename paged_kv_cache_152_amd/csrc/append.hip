@@ -17,38 +17,27 @@ namespace pkv {
 namespace {
 
 // fp32 -> OCP E4M3 ("FN": bias 7, no infinities, S.1111.111 = NaN, max 448),
-// round to nearest, ties to even, values beyond 448 saturate.  Integer-only.
+// round to nearest, ties to even, values beyond 448 saturate.  Branch-free:
+// every case is computed and the right one selected.
+//  - Normal codes (|x| >= 2^-6): re-bias the fp32 exponent from 127 to 7 in
+//    the bit pattern and drop 20 fraction bits, adding 0x7FFFF plus the kept
+//    low bit first, which rounds to nearest even (a carry may step into the
+//    next binade, as the value does).
+//  - Subnormal codes (|x| < 2^-6): the code is k with value k * 2^-9, so
+//    k = rint(|x| * 2^9), exact in fp32 since the scaling is by a power of 2;
+//    k = 8 is the smallest normal code, which is where such a rounding lands.
 __device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
     const uint32_t u = __float_as_uint(x);
     const uint32_t sign = (u >> 24) & 0x80u;
     const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return 0x7Fu;                 // NaN
-    if (a >= 0x43E00000u) return sign | 0x7Eu;         // |x| >= 448 (incl. inf): saturate
-    const uint32_t e32 = a >> 23;                      // biased fp32 exponent
-    if (e32 >= 121u) {                                 // |x| >= 2^-6: E4M3 normal range
-        const uint32_t man = a & 0x7FFFFFu;
-        uint32_t code = ((e32 - 120u) << 3) | (man >> 20);
-        const uint32_t rem = man & 0xFFFFFu;
-        if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ++code;  // carries into exponent
-        return sign | code;                            // code <= 0x7E since |x| < 448
-    }
-    // Subnormal E4M3: value = k * 2^-9, k = round(|x| * 2^9).
-    // |x| = sig * 2^(e - 150) with sig the 24-bit significand (e >= 1) or the raw
-    // fraction (e == 0, where the exponent is that of e == 1).
-    const uint32_t sig = e32 ? ((a & 0x7FFFFFu) | 0x800000u) : (a & 0x7FFFFFu);
-    const uint32_t shift = 141u - (e32 ? e32 : 1u);    // >= 21
-    if (shift >= 25u) return sign;                     // |x| < 2^-10: rounds to zero
-    uint32_t k = sig >> shift;
-    const uint32_t rem = sig & ((1u << shift) - 1u);
-    const uint32_t half = 1u << (shift - 1u);
-    if (rem > half || (rem == half && (k & 1u))) ++k;  // k == 8 is the smallest normal
-    return sign | k;
-}
-
-template <int SRC>
-__device__ __forceinline__ float src_elem(const char* p, int i) {
-    if constexpr (SRC == DT_F32) return reinterpret_cast<const float*>(p)[i];
-    else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);  // bf16
+    const uint32_t rb = a - (120u << 23);
+    const uint32_t nrm = (rb + 0x7FFFFu + ((rb >> 20) & 1u)) >> 20;
+    const float small = __uint_as_float(a < (121u << 23) ? a : (121u << 23));   // |x| clamped to 2^-6
+    const uint32_t sub = (uint32_t)__builtin_rintf(small * 512.0f);             // 0 .. 8
+    uint32_t code = a >= (121u << 23) ? nrm : sub;
+    code = a >= 0x43E00000u ? 0x7Eu : code;            // |x| >= 448 (incl. inf): saturate
+    code |= sign;
+    return a > 0x7F800000u ? 0x7Fu : code;             // NaN
 }
 
 // Same-dtype append: one 16-byte chunk per thread.
@@ -91,14 +80,24 @@ __global__ __launch_bounds__(256) void kv_append_fp8(AppendParams p) {
     if (slot < 0 || (int64_t)slot >= p.num_slots) return;
     const int64_t blk = slot / kBlock, row = slot % kBlock;
     const float inv = (which ? p.v_inv : p.k_inv)[g];
-    const char* src = reinterpret_cast<const char*>(which ? p.v_src : p.k_src) +
-                      (((int64_t)t * p.H_kv + g) * p.D + (int64_t)chunk * 16) * SE;
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(which ? p.v_src : p.k_src) +
+                                                      (((int64_t)t * p.H_kv + g) * p.D + (int64_t)chunk * 16) * SE);
+    uint4 raw[SE];                                     // the chunk's 16 source values, 16-byte loads
+#pragma unroll
+    for (int i = 0; i < SE; ++i) raw[i] = src[i];
+    const uint32_t* rw = reinterpret_cast<const uint32_t*>(raw);
     uint32_t words[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         uint32_t packed = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) packed |= e4m3_from_f32(src_elem<SRC>(src, 4 * w + k) * inv) << (8 * k);
+        for (int k = 0; k < 4; ++k) {
+            const int e = 4 * w + k;
+            float x;
+            if constexpr (SRC == DT_F32) x = __uint_as_float(rw[e]);
+            else x = __uint_as_float(e & 1 ? rw[e >> 1] & 0xFFFF0000u : rw[e >> 1] << 16);   // bf16
+            packed |= e4m3_from_f32(x * inv) << (8 * k);
+        }
         words[w] = packed;
     }
     char* dst = reinterpret_cast<char*>(which ? p.v_pool : p.k_pool) +
