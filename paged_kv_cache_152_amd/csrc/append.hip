@@ -123,14 +123,40 @@ __device__ __forceinline__ uint32_t int8_code(float x, float lo, float hi) {
 
 __device__ __forceinline__ float int8_step(float lo, float hi) { return (hi - lo) / 255.0f; }
 
+// The 16 source values of chunk c (16 consecutive elements) of a token's row,
+// with 16-byte loads: the source is 16-byte aligned and D is a multiple of 16.
 template <int SRC>
-__device__ __forceinline__ float src_value(const void* p, int64_t i) {
-    if constexpr (SRC == DT_F32) return reinterpret_cast<const float*>(p)[i];
-    else if constexpr (SRC == DT_F16) return (float)reinterpret_cast<const _Float16*>(p)[i];
-    else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);
+__device__ __forceinline__ void src_chunk16(const void* p, int64_t row0, int c, float (&x)[16]) {
+    if constexpr (SRC == DT_F32) {
+        const uint4* q = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p) + row0) + 4 * c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 w = q[i];
+            x[4 * i] = __uint_as_float(w.x);
+            x[4 * i + 1] = __uint_as_float(w.y);
+            x[4 * i + 2] = __uint_as_float(w.z);
+            x[4 * i + 3] = __uint_as_float(w.w);
+        }
+    } else {
+        const uint4* q = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + row0) + 2 * c;
+        uint32_t w[8];
+        const uint4 a = q[0], b = q[1];
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (SRC == DT_F16) {
+                x[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+                x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+            } else {                                                   // bf16
+                x[2 * i] = __uint_as_float(w[i] << 16);
+                x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+        }
+    }
 }
 
-// Pass 1: each written slot records (this call's epoch, token).
+// Pass 1 of calls over 64 tokens: each written slot records (this call's
+// epoch, token).
 __global__ __launch_bounds__(256) void kv_append_int8_tag(AppendParams p) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= p.T) return;
@@ -139,18 +165,33 @@ __global__ __launch_bounds__(256) void kv_append_int8_tag(AppendParams p) {
     p.tags[slot] = ((uint64_t)p.epoch << 32) | (uint32_t)t;
 }
 
-// Pass 2: one wave per (token, KV head).  The wave of the lowest token of this
-// call in a tile encodes the whole tile (K, then V); the others exit.  Lane r
-// < 16 learns which token writes row r this call (or none).
-template <int SRC>
+constexpr int kInt8ScanTokens = 64;   // calls up to this many tokens find a tile's writers by a scan
+
+// One wave per (token, KV head, K or V).  The wave of the lowest token of this
+// call in a tile encodes the whole tile; the others exit.  Lane r < 16
+// learns which token writes row r this call (or none): from the slots
+// themselves when the call has at most 64 tokens (SCAN: lane j holds token j's
+// slot; ties between duplicate slots go to the lower token), else from the
+// tags of pass 1.  Work on a tile goes in 16-byte chunks of a row.
+template <int SRC, bool SCAN>
 __global__ __launch_bounds__(64) void kv_append_int8(AppendParams p) {
 #pragma clang fp contract(off)   // a re-encoded value is min + code * step, rounded twice
+    __shared__ int row_writer[kBlock];
     const int t = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
     const int32_t slot = p.slots[t];
     if (slot < 0 || (int64_t)slot >= p.num_slots) return;
     const int64_t blk = slot / kBlock;
     int writer = -1;
-    if (lane < kBlock) {
+    if constexpr (SCAN) {
+        const int32_t s = lane < p.T ? p.slots[lane] : -1;
+        const bool mine = s >= 0 && (int64_t)s < p.num_slots && s / kBlock == blk;
+        const int row = mine ? s % kBlock : kBlock;
+#pragma unroll
+        for (int r = 0; r < kBlock; ++r) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(row == r);
+            if (lane == r && m) writer = __builtin_ctzll(m);
+        }
+    } else if (lane < kBlock) {
         const uint64_t tag = p.tags[blk * kBlock + lane];
         if ((uint32_t)(tag >> 32) == p.epoch) writer = (int)(uint32_t)tag;
     }
@@ -159,23 +200,28 @@ __global__ __launch_bounds__(64) void kv_append_int8(AppendParams p) {
     for (int o = 32; o >= 1; o >>= 1) lowest = min(lowest, __shfl_xor(lowest, o, 64));
     if (lowest != t) return;                             // uniform: another wave owns the tile
     const uint32_t written = (uint32_t)__builtin_amdgcn_ballot_w64(lane < kBlock && writer >= 0) & 0xFFFFu;
+    if (lane < kBlock) row_writer[lane] = writer;
+    __syncthreads();
     const bool fresh = written & 1u;                     // row 0 written: the tile starts over
-    const int D = p.D;
+    const int D = p.D, cpr = D / 16, chunks = kBlock * cpr;
     const int64_t tile = tile_bytes(DT_INT8, D);
-    for (int which = 0; which < 2; ++which) {
+    {
+        const int which = blockIdx.z;                    // 0: K, 1: V
         uint8_t* base = reinterpret_cast<uint8_t*>(which ? p.v_pool : p.k_pool) + (blk * p.H_kv + g) * tile;
+        uint4* base4 = reinterpret_cast<uint4*>(base);
         float* header = reinterpret_cast<float*>(base + (int64_t)kBlock * D);
         const void* src = which ? p.v_src : p.k_src;
         // the range of this call's values in the tile
         float lo = INFINITY, hi = -INFINITY;
-        for (int r = 0; r < kBlock; ++r) {
-            if (!((written >> r) & 1u)) continue;        // uniform
-            const int tr = __shfl(writer, r, 64);
-            const int64_t row0 = ((int64_t)tr * p.H_kv + g) * D;
-            for (int e = lane; e < D; e += 64) {
-                const float x = src_value<SRC>(src, row0 + e);
-                lo = fminf(lo, x);
-                hi = fmaxf(hi, x);
+        for (int c = lane; c < chunks; c += 64) {
+            const int r = c / cpr;
+            if (!((written >> r) & 1u)) continue;
+            float x[16];
+            src_chunk16<SRC>(src, ((int64_t)row_writer[r] * p.H_kv + g) * D, c - r * cpr, x);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                lo = fminf(lo, x[k]);
+                hi = fmaxf(hi, x[k]);
             }
         }
 #pragma unroll
@@ -188,21 +234,40 @@ __global__ __launch_bounds__(64) void kv_append_int8(AppendParams p) {
             const float new_lo = fminf(old_lo, lo), new_hi = fmaxf(old_hi, hi);
             if (new_lo != old_lo || new_hi != old_hi) {  // the range moved: re-encode the other rows
                 const float old_step = int8_step(old_lo, old_hi);
-                for (int i = lane; i < kBlock * D; i += 64) {
-                    const int r = i / D;
-                    if ((written >> r) & 1u) continue;
-                    const float v = old_lo + (float)base[i] * old_step;   // two roundings (contract off)
-                    base[i] = (uint8_t)int8_code(v, new_lo, new_hi);
+                for (int c = lane; c < chunks; c += 64) {
+                    if ((written >> (c / cpr)) & 1u) continue;
+                    uint4 w = base4[c];
+                    uint32_t* wv = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t o = 0;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const float v = old_lo + (float)((wv[i] >> (8 * k)) & 0xFFu) * old_step;  // two roundings
+                            o |= int8_code(v, new_lo, new_hi) << (8 * k);
+                        }
+                        wv[i] = o;
+                    }
+                    base4[c] = w;
                 }
             }
             lo = new_lo;
             hi = new_hi;
         }
-        for (int r = 0; r < kBlock; ++r) {
+        for (int c = lane; c < chunks; c += 64) {
+            const int r = c / cpr;
             if (!((written >> r) & 1u)) continue;
-            const int tr = __shfl(writer, r, 64);
-            const int64_t row0 = ((int64_t)tr * p.H_kv + g) * D;
-            for (int e = lane; e < D; e += 64) base[r * D + e] = (uint8_t)int8_code(src_value<SRC>(src, row0 + e), lo, hi);
+            float x[16];
+            src_chunk16<SRC>(src, ((int64_t)row_writer[r] * p.H_kv + g) * D, c - r * cpr, x);
+            uint32_t wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t o = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) o |= int8_code(x[4 * i + k], lo, hi) << (8 * k);
+                wv[i] = o;
+            }
+            base4[c] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
         }
         if (lane == 0) {
             header[0] = lo;
@@ -283,15 +348,22 @@ hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream) {
     if (p.T <= 0) return hipSuccess;
     AppendParams arg = p;
     if (p.dst_dt == DT_INT8) {
-        if (!p.tags || p.epoch == 0) return hipErrorInvalidValue;
+        if (!p.tags || p.epoch == 0 || p.D % 16) return hipErrorInvalidValue;
         void* args[] = {&arg};
-        hipError_t e = launch_kernel(reinterpret_cast<const void*>(kv_append_int8_tag),
-                                       dim3((unsigned)((p.T + 255) / 256)), dim3(256), args, 0, stream);
-        if (e != hipSuccess) return e;
-        const void* fn = p.src_dt == DT_F32   ? reinterpret_cast<const void*>(kv_append_int8<DT_F32>)
-                         : p.src_dt == DT_F16 ? reinterpret_cast<const void*>(kv_append_int8<DT_F16>)
-                                              : reinterpret_cast<const void*>(kv_append_int8<DT_BF16>);
-        return launch_kernel(fn, dim3((unsigned)p.T, (unsigned)p.H_kv), dim3(64), args, 0, stream);
+        const bool scan = p.T <= kInt8ScanTokens;
+        if (!scan) {
+            hipError_t e = launch_kernel(reinterpret_cast<const void*>(kv_append_int8_tag),
+                                         dim3((unsigned)((p.T + 255) / 256)), dim3(256), args, 0, stream);
+            if (e != hipSuccess) return e;
+        }
+        const void* fn =
+            scan ? (p.src_dt == DT_F32   ? reinterpret_cast<const void*>(kv_append_int8<DT_F32, true>)
+                    : p.src_dt == DT_F16 ? reinterpret_cast<const void*>(kv_append_int8<DT_F16, true>)
+                                         : reinterpret_cast<const void*>(kv_append_int8<DT_BF16, true>))
+                 : (p.src_dt == DT_F32   ? reinterpret_cast<const void*>(kv_append_int8<DT_F32, false>)
+                    : p.src_dt == DT_F16 ? reinterpret_cast<const void*>(kv_append_int8<DT_F16, false>)
+                                         : reinterpret_cast<const void*>(kv_append_int8<DT_BF16, false>));
+        return launch_kernel(fn, dim3((unsigned)p.T, (unsigned)p.H_kv, 2), dim3(64), args, 0, stream);
     }
     if (p.dst_dt == p.src_dt) {
         int row_bytes = p.D * elem_bytes(p.dst_dt);

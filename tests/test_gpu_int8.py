@@ -149,6 +149,30 @@ def test_int8_decode_vs_oracle(q_dt, D, G):
     c.pool.close()
 
 
+def test_int8_ragged_calls_into_partial_tiles():
+    """Calls of 1 to 99 tokens, several tokens per tile, into partly filled
+    tiles: both ways a wave finds its tile's writers (a scan of the call's
+    slots up to 64 tokens, the tag pass above) widen and re-encode tiles as
+    the model does."""
+    c = Int8Case(2, 64, [0] * 5, wl.BF16, seed=700, num_blocks=400)
+    r = np.random.default_rng(701)
+    sizes = []
+    for _ in range(30):
+        which = sorted(r.choice(5, size=r.integers(1, 6), replace=False).tolist())
+        n = int(r.choice([1, 2, 3, 7, 13, 33]))
+        c.append(which, n)
+        sizes.append(len(which) * n)
+    assert min(sizes) <= 64 < max(sizes)
+    c.lens = list(c.cur)
+    rows = c.check_tiles()
+    q = c.query(5, 8, wl.BF16, seed=702)
+    scale = 0.125
+    err = parity_error(c.decode(q, wl.BF16, scale), c.expected(q, wl.BF16, scale), wl.BF16)
+    say(f"int8 ragged calls {sorted(sizes)}: {rows} rows bit-exact, decode err {err:.2e}")
+    assert err <= TOL[wl.INT8]
+    c.pool.close()
+
+
 def test_int8_many_partitions():
     """Long contexts: the planned multi-partition path (work list + merge)."""
     c = Int8Case(2, 128, [9000, 5000, 700, 6100], wl.BF16, seed=300, prefill_frac=0.99)
