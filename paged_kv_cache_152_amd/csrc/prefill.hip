@@ -489,36 +489,46 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 // before the data has landed.  In asm because the compiler, unable to tell
 // these reads from the stage loads still landing in other LDS buffers, would
 // otherwise drain every outstanding vector-memory load first.
-template <int OFF>
+// The reads sit at a + BASE and a + BASE + OFF (immediate offsets, so a stage
+// buffer known at compile time costs no address arithmetic).
+template <int BASE, int OFF>
 __device__ __forceinline__ void tr_issue8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x2_t (&o)[8]) {
+    static_assert(BASE >= 0 && BASE + OFF < 65536, "16-bit LDS offset");
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %2, %9\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %4, %10\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %6, %11\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:%12"
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13"
         : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
-        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(OFF)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(BASE), "n"(BASE + OFF)
         : "memory");
 }
-// Eight ds_read_b64_tr_b8 at a[0..7], issued without waiting (tr_wait8 waits).
+// Eight ds_read_b64_tr_b8 at a[0..7] + BASE, issued without waiting (tr_wait8 waits).
+template <int BASE>
 __device__ __forceinline__ void trb8_issue8(const uint32_t (&a)[8], u32x2_t (&o)[8]) {
+    static_assert(BASE >= 0 && BASE < 65536, "16-bit LDS offset");
     asm volatile(
-        "ds_read_b64_tr_b8 %0, %8\n\t"
-        "ds_read_b64_tr_b8 %1, %9\n\t"
-        "ds_read_b64_tr_b8 %2, %10\n\t"
-        "ds_read_b64_tr_b8 %3, %11\n\t"
-        "ds_read_b64_tr_b8 %4, %12\n\t"
-        "ds_read_b64_tr_b8 %5, %13\n\t"
-        "ds_read_b64_tr_b8 %6, %14\n\t"
-        "ds_read_b64_tr_b8 %7, %15"
+        "ds_read_b64_tr_b8 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %7, %15 offset:%16"
         : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "n"(BASE)
         : "memory");
 }
+
+template <int V>
+struct StageBuf {
+    static constexpr int value = V;
+};
 __device__ __forceinline__ void tr_wait8(u32x2_t (&o)[8]) {
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]), "+v"(o[6]), "+v"(o[7])
@@ -669,9 +679,10 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     }
 
     const int wg_min_see = p.causal ? n - q_len + tile0 : n - 1;
-    auto compute = [&](bool masked, int j, int buf) {
+    auto compute = [&](bool masked, int j, auto BUF) {
+        constexpr int buf = decltype(BUF)::value;
         const unsigned char* kt = k_lds[buf];
-        const unsigned char* vt = v_lds[buf];
+        const unsigned char* vt = v_lds[0];        // V reads: buffer 0's address + buf * SB as an immediate
         // K operand of block h: token c, dims 32 k + 8 r .. +7 (16 bytes, or 8
         // E4M3 codes widened exactly to q's type)
         QV ka[2][KS];
@@ -713,7 +724,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
                 uint32_t a8[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) a8[u] = rbase + (uint32_t)(((m8 + u) ^ sw) * 16);
-                trb8_issue8(a8, vh[m8 / 8]);
+                trb8_issue8<buf * SB>(a8, vh[m8 / 8]);
             }
         } else {
             const int vrow = 4 * r + (c >> 2);
@@ -727,7 +738,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
                     const int lc = 2 * (m4 + u) + ((c & 3) >> 1);
                     a[u] = vrow_addr + (uint32_t)((lc ^ chunk_swizzle<SWZ>(vrow)) * 16);
                 }
-                tr_issue8<kBlock * ROWB>(a[0], a[1], a[2], a[3], vh[m4 / 4]);
+                tr_issue8<buf * SB, kBlock * ROWB>(a[0], a[1], a[2], a[3], vh[m4 / 4]);
             }
         }
         const int tok = 2 * j * kBlock + 4 * r;
@@ -800,17 +811,25 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     // chunk workload).  The pair j, j + 1 was issued two stages earlier; once
     // it has landed, the barrier also means every wave is done with the
     // previous pair's buffers, which the next pair then refills.
+    // The loop is unrolled over the four buffers, so that each stage's LDS
+    // addresses are loop-invariant registers plus immediate offsets.
     static_assert(kStages == 4, "two pairs of stage buffers");
-    if (n_it > 0) issue(0);
-    if (n_it > 1) issue(1);
-    for (int j = 0; j < n_it; ++j) {
-        if ((j & 1) == 0) {
+    auto step = [&](int j, auto BUF) {
+        if constexpr (decltype(BUF)::value % 2 == 0) {
             wait_loads_then_barrier<0>();
             if (j + 2 < n_it) issue(j + 2);
             if (j + 3 < n_it) issue(j + 3);
         }
         const int t0 = 2 * j * kBlock;
-        compute(!(t0 + 2 * kBlock <= n && t0 + 2 * kBlock - 1 <= wg_min_see), j, j % kStages);
+        compute(!(t0 + 2 * kBlock <= n && t0 + 2 * kBlock - 1 <= wg_min_see), j, BUF);
+    };
+    if (n_it > 0) issue(0);
+    if (n_it > 1) issue(1);
+    for (int j = 0; j < n_it; j += kStages) {
+        step(j, StageBuf<0>{});
+        if (j + 1 < n_it) step(j + 1, StageBuf<1>{});
+        if (j + 2 < n_it) step(j + 2, StageBuf<2>{});
+        if (j + 3 < n_it) step(j + 3, StageBuf<3>{});
     }
 
     uint16_t* o16 = reinterpret_cast<uint16_t*>(p.out);
