@@ -451,13 +451,18 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
 
 // Max across the four lanes of a row (l % 16 equal): v_permlane16_swap pairs
 // row r with row r ^ 1 (lanes 16 apart), v_permlane32_swap pairs r with r ^ 2.
+// After a swap of a value with itself, the two results hold, in every lane,
+// that lane's value and its partner's (16 or 32 lanes away), so their max is
+// the pair's max and the value itself need not be kept alive for it (one
+// register copy per swap instead of two).
 __device__ __forceinline__ float row_max4(float v) {
     const uint32_t u = __builtin_bit_cast(uint32_t, v);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const float m = vmax3(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]), v);
+    const float m = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)a[0]),
+                                                  __builtin_bit_cast(float, (uint32_t)a[1]));
     const uint32_t w = __builtin_bit_cast(uint32_t, m);
     const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return vmax3(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]), m);
+    return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
 }
 
 __device__ __forceinline__ float row_sum4(float v) {
