@@ -674,10 +674,14 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     };
 
     f32x4_t acc[R][MT];
-    float m_run[R], l_run[R];
+    // m_run is the reference max; neg_m (its negation, 0 while it is -inf) and
+    // thr (the level a block max must pass to move it) change only with it.
+    float m_run[R], l_run[R], neg_m[R], thr[R];
 #pragma unroll
     for (int rg = 0; rg < R; ++rg) {
         m_run[rg] = -INFINITY;
+        neg_m[rg] = 0.0f;
+        thr[rg] = -INFINITY + kLazy;
         l_run[rg] = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -766,18 +770,19 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
             }
             const float mx = vmax3(vmax3(z[0], z[1], z[2]), vmax3(z[3], z[4], z[5]), vmax3(z[6], z[7], z[7]));
             const float m_blk = row_max4(mx) * qscale;
-            if (__builtin_amdgcn_ballot_w64(m_blk > m_run[rg] + kLazy) != 0) {
-                const float m_new = m_blk > m_run[rg] + kLazy ? m_blk : m_run[rg];
+            if (__builtin_amdgcn_ballot_w64(m_blk > thr[rg]) != 0) {
+                const float m_new = m_blk > thr[rg] ? m_blk : m_run[rg];
                 const float alpha = m_new == m_run[rg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
                 l_run[rg] *= alpha;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc[rg][mt] *= alpha;
                 m_run[rg] = m_new;
+                neg_m[rg] = m_new == -INFINITY ? 0.0f : -m_new;
+                thr[rg] = m_new + kLazy;
             }
-            const float neg_m = m_run[rg] == -INFINITY ? 0.0f : -m_run[rg];
             float pr[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(z[i], qscale, neg_m));
+            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(z[i], qscale, neg_m[rg]));
             // l sums the rounded weights P.V multiplies (a normalised average of
             // them); each lane keeps the part of its own tokens, all four lanes of
             // a row rescale alike, and the parts are added at the end
