@@ -465,6 +465,26 @@ __device__ __forceinline__ float row_max4(float v) {
     return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
 }
 
+// row_max4 of two values a, b at once.  A 32-lane swap of a against b leaves
+// a's lanes 0-31 and b's lanes 0-31 in the first result and both upper halves
+// in the second, so their max holds a's pair max (lanes l, l + 32) in lanes
+// 0-31 and b's in lanes 32-63; a 16-lane swap of that with itself completes
+// both four-lane maxes, and a last 32-lane swap copies each half across.
+__device__ __forceinline__ void row_max4x2(float a, float b, float& ma, float& mb) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                    false, false);
+    const float c = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)s[0]),
+                                                  __builtin_bit_cast(float, (uint32_t)s[1]));
+    const uint32_t cu = __builtin_bit_cast(uint32_t, c);
+    const auto t = __builtin_amdgcn_permlane16_swap(cu, cu, false, false);
+    const float d = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)t[0]),
+                                                  __builtin_bit_cast(float, (uint32_t)t[1]));
+    const uint32_t du = __builtin_bit_cast(uint32_t, d);
+    const auto u = __builtin_amdgcn_permlane32_swap(du, du, false, false);
+    ma = __builtin_bit_cast(float, (uint32_t)u[0]);
+    mb = __builtin_bit_cast(float, (uint32_t)u[1]);
+}
+
 __device__ __forceinline__ float row_sum4(float v) {
     const uint32_t u = __builtin_bit_cast(uint32_t, v);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -752,6 +772,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         }
         const int tok = 2 * j * kBlock + 4 * r;
         PV pb[R];
+        float z[R][8], mx[R];
 #pragma unroll
         for (int rg = 0; rg < R; ++rg) {
             f32x4_t S0 = {0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
@@ -760,16 +781,27 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
                 S0 = mma_k32<QDT>(ka[0][k], qb[rg][k], S0);
                 S1 = mma_k32<QDT>(ka[1][k], qb[rg][k], S1);
             }
-            float z[8] = {S0[0], S0[1], S0[2], S0[3], S1[0], S1[1], S1[2], S1[3]};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                z[rg][i] = S0[i];
+                z[rg][4 + i] = S1[i];
+            }
             if (masked) {
                 // token tok + (i / 4) * 16 + i % 4 is visible iff that offset <= lim
                 const int lim = min(n - 1, see[rg]) - tok;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    z[i] = (i >> 2) * kBlock + (i & 3) <= lim ? z[i] : -INFINITY;   // select, never 0 * garbage
+                    z[rg][i] = (i >> 2) * kBlock + (i & 3) <= lim ? z[rg][i] : -INFINITY;   // select, never 0 * garbage
             }
-            const float mx = vmax3(vmax3(z[0], z[1], z[2]), vmax3(z[3], z[4], z[5]), vmax3(z[6], z[7], z[7]));
-            const float m_blk = row_max4(mx) * qscale;
+            mx[rg] = vmax3(vmax3(z[rg][0], z[rg][1], z[rg][2]), vmax3(z[rg][3], z[rg][4], z[rg][5]),
+                           vmax3(z[rg][6], z[rg][7], z[rg][7]));
+        }
+        static_assert(R == 2, "row maxes are reduced in pairs");
+        float rmax[R];
+        row_max4x2(mx[0], mx[1], rmax[0], rmax[1]);
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) {
+            const float m_blk = rmax[rg] * qscale;
             if (__builtin_amdgcn_ballot_w64(m_blk > thr[rg]) != 0) {
                 const float m_new = m_blk > thr[rg] ? m_blk : m_run[rg];
                 const float alpha = m_new == m_run[rg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
@@ -782,7 +814,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
             }
             float pr[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(z[i], qscale, neg_m[rg]));
+            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(z[rg][i], qscale, neg_m[rg]));
             // l sums the rounded weights P.V multiplies (a normalised average of
             // them); each lane keeps the part of its own tokens, all four lanes of
             // a row rescale alike, and the parts are added at the end
