@@ -786,16 +786,21 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
                 z[rg][i] = S0[i];
                 z[rg][4 + i] = S1[i];
             }
-            if (masked) {
+        }
+        if (masked) {                          // one uniform branch for both row groups
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg) {
                 // token tok + (i / 4) * 16 + i % 4 is visible iff that offset <= lim
                 const int lim = min(n - 1, see[rg]) - tok;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     z[rg][i] = (i >> 2) * kBlock + (i & 3) <= lim ? z[rg][i] : -INFINITY;   // select, never 0 * garbage
             }
+        }
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg)
             mx[rg] = vmax3(vmax3(z[rg][0], z[rg][1], z[rg][2]), vmax3(z[rg][3], z[rg][4], z[rg][5]),
                            vmax3(z[rg][6], z[rg][7], z[rg][7]));
-        }
         static_assert(R == 2, "row maxes are reduced in pairs");
         float rmax[R];
         row_max4x2(mx[0], mx[1], rmax[0], rmax[1]);
