@@ -197,22 +197,25 @@ def test_prefill_deterministic():
     c.close()
 
 
-def test_prefill_long_context_sampled():
-    """2 sequences of 2048 cached tokens plus a 512-token chunk, Llama-3-8B heads:
-    sampled rows against the oracle (a row at position p is the one-token chunk
-    with context p + 1)."""
-    c = Case(wl.BF16, 32, 8, 128, [(2560, 512), (2304, 256)], seed=11)
+@pytest.mark.parametrize("kv_dt", [wl.BF16, wl.E4M3])
+def test_prefill_long_context_sampled(kv_dt):
+    """2 sequences of 2048 cached tokens plus a 512-token chunk, Llama-3-8B heads
+    (the prefill8b shape, and prefill8b_fp8 with an FP8 pool): sampled rows
+    against the oracle (a row at position p is the one-token chunk with
+    context p + 1)."""
+    c = Case(kv_dt, 32, 8, 128, [(2560, 512), (2304, 256)], seed=11)
     got = c.run()
     K, V = c.oracle_kv()
+    kw = dict(k_scale=c.scales[0], v_scale=c.scales[1]) if c.scales else {}
     off = [0, int(c.lens[0])]
     rows = [0, 1, 255, 256, 511, 512, 700, 767]
     for t in rows:
         s = 0 if t < c.q_start[1] else 1
         i = t - c.q_start[s]
         p = int(c.lens[s]) - int(c.q_lens[s]) + i
-        want = oracle.prefill_attention(c.q[t:t + 1], wl.BF16, [0, 1], K, V, wl.BF16, [off[s]], [p + 1],
-                                        c.scale)
-        check(got[t:t + 1], want, wl.BF16, wl.BF16, f"row {t}")
+        want = oracle.prefill_attention(c.q[t:t + 1], c.q_dt, [0, 1], K, V, kv_dt, [off[s]], [p + 1],
+                                        c.scale, **kw)
+        check(got[t:t + 1], want, kv_dt, c.q_dt, f"row {t}")
     c.close()
 
 
