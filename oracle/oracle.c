@@ -89,22 +89,19 @@ double oracle_e4m3_to_f64(uint8_t c) {
  * OCP saturating conversion require.  NaN becomes 0x7F.  Written as a search
  * over the 127 non-negative finite codes, which are increasing in value. */
 uint8_t oracle_e4m3_from_f32(float x) {
-    static double mag[127];
-    static int ready = 0;
-    if (!ready) {            /* idempotent fill; every thread writes identical values */
-        for (int c = 0; c < 127; ++c) mag[c] = oracle_e4m3_to_f64((uint8_t)c);
-        ready = 1;
-    }
     if (isnan(x)) return 0x7F;
     uint8_t sign = signbit(x) ? 0x80 : 0x00;
     double a = fabs((double)x);
     if (a >= 448.0) return (uint8_t)(sign | 0x7E);
-    int lo = 0, hi = 126;    /* invariant: mag[lo] <= a < mag[hi] */
+    /* No table and no static state: the search decodes the codes it visits, so
+     * the function is safe to call from any number of threads at once. */
+    int lo = 0, hi = 126;    /* invariant: value(lo) <= a < value(hi) */
     while (hi - lo > 1) {
         int mid = (lo + hi) / 2;
-        if (mag[mid] <= a) lo = mid; else hi = mid;
+        if (oracle_e4m3_to_f64((uint8_t)mid) <= a) lo = mid; else hi = mid;
     }
-    double dlo = a - mag[lo], dhi = mag[hi] - a;           /* both exact in double */
+    double dlo = a - oracle_e4m3_to_f64((uint8_t)lo);      /* both exact in double */
+    double dhi = oracle_e4m3_to_f64((uint8_t)hi) - a;
     int c;
     if (dlo < dhi) c = lo;
     else if (dhi < dlo) c = hi;
@@ -114,7 +111,6 @@ uint8_t oracle_e4m3_from_f32(float x) {
 
 /* Array forms, so the harness does not loop in Python. */
 void oracle_e4m3_encode_f32_array(const float* x, int64_t n, uint8_t* out, int32_t nthreads) {
-    (void)oracle_e4m3_from_f32(0.0f);                      /* fill the table once */
 #ifdef _OPENMP
 #pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads())
 #endif
