@@ -150,3 +150,30 @@ class TileStore:
             rows = min(BLOCK, n - BLOCK * j)
             out[BLOCK * j:BLOCK * j + rows] = value(codes[:, :rows], lo[:, None, None], hi[:, None, None]).transpose(1, 0, 2)
         return out
+
+
+def one_shot_values(x) -> np.ndarray:
+    """The page's formula applied once per (16-row tile, KV head) over the rows
+    the tile finally holds -- the plain definition, independent of how appends
+    filled the tile.
+
+    x: [n][H_kv][D] values of one sequence in logical order (any float type).
+    Tile j holds rows 16j .. min(16j + 16, n) - 1.  For each tile and head, in
+    fp64: k_min, k_max over the tile's rows and dims, q = round-half-even(
+    (x - k_min) / (k_max - k_min) * 255), and the value a code stands for,
+    k_min + q * (k_max - k_min) / 255, evaluated as (k_min * (255 - q) +
+    k_max * q) / 255 so that codes 0 and 255 give k_min and k_max exactly for
+    fp32-representable inputs.  A constant tile (k_max == k_min) stands for
+    its constant.  Returns fp64 [n][H_kv][D]."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[0]
+    out = np.empty_like(x)
+    for j0 in range(0, n, BLOCK):
+        tile = x[j0:j0 + BLOCK]                                # [rows][H][D]
+        k_min = tile.min(axis=(0, 2))[None, :, None]
+        k_max = tile.max(axis=(0, 2))[None, :, None]
+        span = k_max - k_min
+        flat = span == 0
+        q = np.rint((tile - k_min) / np.where(flat, 1.0, span) * 255.0)
+        out[j0:j0 + BLOCK] = np.where(flat, tile, (k_min * (255.0 - q) + k_max * q) / 255.0)
+    return out

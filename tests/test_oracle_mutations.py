@@ -72,9 +72,18 @@ I8_MUTANTS = {
     "int8_range_not_widened": ("lo, hi = np.minimum(old_lo, lo), np.maximum(old_hi, hi)", "lo, hi = lo, hi",
                                [pins.check_int8_fill_invariants]),
     "int8_no_reencode": ("codes[h, rest] = encode(value_f32(codes[h, rest], old_lo[h], old_hi[h]), lo[h], hi[h])",
-                         "pass", [pins.check_int8_fill_invariants]),
+                         "pass", [pins.check_int8_fill_invariants, pins.check_int8_token_fill_vs_one_shot]),
     "int8_reencode_reads_new_range": ("value_f32(codes[h, rest], old_lo[h], old_hi[h])",
-                                      "value_f32(codes[h, rest], lo[h], hi[h])", [pins.check_int8_fill_invariants]),
+                                      "value_f32(codes[h, rest], lo[h], hi[h])",
+                                      [pins.check_int8_fill_invariants, pins.check_int8_token_fill_vs_one_shot]),
+    "one_shot_range_over_sequence": ("k_min = tile.min(axis=(0, 2))[None, :, None]",
+                                     "k_min = x.min(axis=(0, 2))[None, :, None]", [pins.check_int8_one_shot]),
+    "one_shot_heads_share_a_range": ("k_max = tile.max(axis=(0, 2))[None, :, None]", "k_max = tile.max()",
+                                     [pins.check_int8_one_shot]),
+    "one_shot_scale_256": ("* 255.0)\n", "* 256.0)\n", [pins.check_int8_one_shot]),
+    "one_shot_truncates": ("q = np.rint(", "q = np.floor(", [pins.check_int8_one_shot]),
+    "one_shot_value_reversed": ("(k_min * (255.0 - q) + k_max * q)", "(k_max * (255.0 - q) + k_min * q)",
+                                [pins.check_int8_one_shot]),
     "int8_heads_share_a_range": ("lo, hi = new.min(axis=(1, 2)), new.max(axis=(1, 2))",
                                  "lo, hi = np.full(self.H_kv, new.min()), np.full(self.H_kv, new.max())",
                                  [pins.check_int8_fill_invariants]),

@@ -530,6 +530,90 @@ def check_int8_fill_invariants(m=_i8):
             assert lo == K[0, g].min() and hi == K[0, g].max()
 
 
+def check_int8_one_shot(m=_i8):
+    """The page's formula applied once per (tile, head): closed forms, the
+    rational formula with round-half-even, half a step of error, and tiles and
+    heads that never see each other's values."""
+    # a tile holding exactly the grid k_min + k * (k_max - k_min) / 255 maps onto itself
+    grid = np.arange(256, dtype=np.float64).reshape(16, 1, 16) * 0.5 - 3.0     # -3 .. 124.5 step 0.5
+    assert np.array_equal(m.one_shot_values(grid), grid)
+    # constant tile: its constant; a lone row of one value too
+    const = np.full((16, 2, 8), 0.7)
+    assert np.array_equal(m.one_shot_values(const), const)
+    rng = np.random.default_rng(45)
+    # dyadic values: every fp64 step of the formula is exact, so the codes equal
+    # the rational formula with round-half-even (ties included)
+    for trial in range(20):
+        x = rng.integers(-64, 65, size=(16, 1, 4)).astype(np.float64) / 8.0
+        x[0, 0, 0], x[1, 0, 0] = -8.0, 8.0                                       # span 16: exact /255 steps
+        v = m.one_shot_values(x)
+        lo, hi = Fraction(-8), Fraction(8)
+        for xi, vi in zip(x.reshape(-1), v.reshape(-1)):
+            q = _half_even((Fraction(float(xi)) - lo) / (hi - lo) * 255)
+            assert float(vi) == float(lo + q * (hi - lo) / 255), (xi, vi, q)   # both correctly rounded
+    # random tiles: within half a step of the input, ends exact, a partial last
+    # tile ranges over its own rows only, heads are independent
+    for n in (1, 15, 16, 17, 40, 77):
+        x = (rng.standard_normal((n, 3, 8)) * np.array([1.0, 10.0, 0.01])[None, :, None]).astype(np.float32)
+        x = x.astype(np.float64)                                                 # fp32 values, as the pools hold
+        v = m.one_shot_values(x)
+        for j0 in range(0, n, 16):
+            t, tv = x[j0:j0 + 16], v[j0:j0 + 16]
+            for h in range(3):
+                lo, hi = t[:, h].min(), t[:, h].max()
+                assert np.all(np.abs(tv[:, h] - t[:, h]) <= (hi - lo) / 510 * (1 + 1e-9))
+                assert tv[:, h].min() == lo and tv[:, h].max() == hi
+            assert np.array_equal(m.one_shot_values(t), tv)                      # the tile alone
+        y = x.copy()
+        y[:, 1] *= 1000.0
+        if n > 16:
+            y[16:32, 0] += 5.0                                                   # another tile of head 0
+        w = m.one_shot_values(y)
+        assert np.array_equal(w[:, 2], v[:, 2]) and np.array_equal(w[:16, 0], v[:16, 0])
+
+
+def _ranges_after_each_row(col):
+    """(k_min, k_max) of rows 0..t of one head's tile, for every t (raw values)."""
+    flat = col.reshape(col.shape[0], -1)
+    return np.minimum.accumulate(flat.min(axis=1)), np.maximum.accumulate(flat.max(axis=1))
+
+
+def check_int8_token_fill_vs_one_shot(m=_i8):
+    """Tiles filled one token per call (the decode pattern), with the model of
+    the appends: every dequantised value lies within the sum of half steps of
+    the ranges its row lived under (counted from the raw data alone: one for
+    its own write, one per later range move) of its raw value, and within that
+    plus half a final step of the page's one-shot value.  Returns the largest
+    errors against the raw values (token fill, one-shot)."""
+    rng = np.random.default_rng(46)
+    H, D, n = 2, 64, 16 * 12 + 5
+    worst_fill = worst_once = 0.0
+    for trial in range(4):
+        X = {kind: (rng.standard_normal((n, H, D)) * rng.choice([0.3, 1.0, 3.0])).astype(np.float32) for kind in "kv"}
+        store = m.TileStore(H, D)
+        for t in range(n):
+            store.append(np.array([t]), X["k"][t:t + 1], X["v"][t:t + 1])
+        blocks = np.arange(-(-n // 16))
+        for kind in "kv":
+            x = X[kind].astype(np.float64)
+            lib = store.values(kind, blocks, n)
+            once = m.one_shot_values(x)
+            for j0 in range(0, n, 16):
+                rows = min(16, n - j0)
+                for h in range(H):
+                    lo, hi = _ranges_after_each_row(x[j0:j0 + rows, h])
+                    half = (hi - lo) / 510.0 * (1 + 1e-4) + 1e-6 * np.maximum(np.abs(lo), np.abs(hi))
+                    moved = np.r_[False, (lo[1:] != lo[:-1]) | (hi[1:] != hi[:-1])]
+                    for r in range(rows):
+                        bound = half[r] + half[r + 1:][moved[r + 1:]].sum()
+                        err = np.abs(lib[j0 + r, h] - x[j0 + r, h]).max()
+                        assert err <= bound, (trial, kind, j0, h, r, err, bound)
+                        assert np.abs(lib[j0 + r, h] - once[j0 + r, h]).max() <= bound + half[-1]
+            worst_fill = max(worst_fill, float(np.abs(lib - x).max() / x.std()))
+            worst_once = max(worst_once, float(np.abs(once - x).max() / x.std()))
+    return worst_fill, worst_once
+
+
 def check_f64_storage_path():
     """Attention on fp64 storage: equal to fp32 storage of the same values, and
     to the textbook softmax on values that fp32 cannot hold."""
@@ -558,6 +642,17 @@ def test_int8_round_trip_half_step():
 
 def test_int8_fill_invariants():
     check_int8_fill_invariants()
+
+
+def test_int8_one_shot_formula():
+    check_int8_one_shot()
+
+
+def test_int8_token_fill_within_its_bound_of_raw_and_one_shot():
+    fill, once = check_int8_token_fill_vs_one_shot()
+    # the token-at-a-time fill drifts further than one quantisation, but stays
+    # within the sum of its own half steps (asserted per element above)
+    assert once < fill < 16 * once
 
 
 def test_int8_tile_store_rename():
