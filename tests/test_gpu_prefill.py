@@ -18,7 +18,7 @@ import harness
 import oracle
 import paged_kv_cache_152_amd as pkv
 import workloads as wl
-from tests.oracle_ref import TOL, fp8_codes, parity_error
+from tests.oracle_ref import TOL, error_beyond_output_rounding, fp8_codes
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -101,10 +101,13 @@ class Case:
 
 
 def check(got, want, kv_dt, q_dt, what):
+    """Error beyond the output format's rounding <= TOL (the prefill rule: the
+    weights enter P.V in q's 16-bit format); the raw max-abs is reported."""
     assert np.isfinite(got).all(), f"{what}: non-finite output"
-    err = parity_error(got, want, q_dt)
-    assert err <= TOL[kv_dt], f"{what}: err {err:.3e} > {TOL[kv_dt]:.0e}"
-    return err
+    err = error_beyond_output_rounding(got, want, q_dt)
+    raw = float(np.abs(got - want).max()) if got.size else 0.0
+    assert err <= TOL[kv_dt], f"{what}: err {err:.3e} beyond output rounding (raw {raw:.3e}) > {TOL[kv_dt]:.0e}"
+    return raw
 
 
 SHAPES = [(37, 37), (300, 45), (129, 1), (64, 16), (17, 3)]
