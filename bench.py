@@ -369,6 +369,8 @@ def main():
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-companion", action="store_true",
+                    help="mha7b: skip the gqa8b figures that are otherwise measured in the same run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
@@ -380,11 +382,33 @@ def main():
     if args.workload == "swap":
         return bench_swap(args)
 
+    w = wl.make(args.workload)
+    result = measure_decode(w, args)
+    if args.workload == "mha7b" and not args.no_companion:
+        # the second target shape, measured in the same run (no CPU leg, no copy probe)
+        g = measure_decode(wl.make("gqa8b"), args, spread=False)
+        result["companion"] = {"gqa8b": {k: g[k] for k in (
+            "value", "unit", "ms_per_step", "pct_of_hbm_peak", "decode_tokens_per_s_per_layer", "kv_bytes_per_step",
+            "decode_only_us", "kernels_us", "roofline", "partition_kernel", "config")}}
+        log(f"[bench] gqa8b: {g['ms_per_step'] * 1e3:.1f} us/step, paged_decode {g['decode_only_us']:.1f} us "
+            f"= {100 * g['roofline']['frac']:.1f}% of 8 TB/s")
+    result["copy_probe_GBps"] = round(copy_probe_gbs(), 1)
+    log(f"[bench] plain copy kernel: {result['copy_probe_GBps']} GB/s (read + write)")
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def measure_decode(w: wl.Workload, args, spread: bool = True) -> dict:
+    """Fill a pool with workload w, time K decode steps (after W warm-ups), then
+    the same K steps again with per-kernel events.  Returns the bench record
+    without the copy probe and the CPU baseline."""
     import torch
     import harness
-    import paged_kv_cache_152_amd as pkv
 
-    w = wl.make(args.workload)
     log(f"[bench] workload {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} D={w.D} "
         f"kv={wl.DTYPE_NAMES[w.kv_dtype]} blocks={w.num_blocks} tokens={int(w.lens.sum())}")
     t0 = time.time()
@@ -426,9 +450,11 @@ def main():
     torch.cuda.synchronize()
     stats = pool.profile_read()
     pool.profile_enable(False)
-    step_dist = {m: per_step_us(torch, prep, out, ws, stream, args.steps, m) for m in ("warm", "cold", "after_write")}
-    log("[bench] per-step p10/p50/p90 (us): " +
-        ", ".join(f"{m} {d['p10']}/{d['p50']}/{d['p90']}" for m, d in step_dist.items()))
+    step_dist = None
+    if spread:
+        step_dist = {m: per_step_us(torch, prep, out, ws, stream, args.steps, m) for m in ("warm", "cold", "after_write")}
+        log("[bench] per-step p10/p50/p90 (us): " +
+            ", ".join(f"{m} {d['p10']}/{d['p50']}/{d['p90']}" for m, d in step_dist.items()))
 
     kv_bytes = w.kv_bytes_per_step()
     kern = {k: {"launches": v["launches"], "timed": v["launches"] - v["dropped"],
@@ -437,7 +463,9 @@ def main():
     part_us = kern.get("paged_decode_partition", {}).get("avg_us")
     red_us = kern.get("paged_decode_reduce", {}).get("avg_us", 0.0)
     plan_us = kern.get("paged_decode_plan", {}).get("avg_us", 0.0)
-    achieved = kv_bytes / (part_us * 1e-6) / 1e9 if part_us else None
+    decode_us = (part_us or 0) + (red_us or 0) + plan_us
+    achieved = kv_bytes / (decode_us * 1e-6) / 1e9 if decode_us else None
+    part_gbs = kv_bytes / (part_us * 1e-6) / 1e9 if part_us else None
     traffic = traffic_for(w.name, "paged_decode_partition", P)
     result = {
         "metric": METRIC,
@@ -461,26 +489,27 @@ def main():
         "kv_bytes_per_step": kv_bytes,
         "pct_of_hbm_peak": round(100 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "kernels_us": kern,
-        "decode_only_us": round((part_us or 0) + (red_us or 0) + plan_us, 3),
+        "decode_only_us": round(decode_us, 3),
         "step_us": step_dist,
-        "host_alloc_us_per_step": round(host_alloc_us(w), 2),
+        "host_alloc_us_per_step": round(host_alloc_us(w), 2) if spread else None,
+        # paged_decode as a whole: the plan, partition and reduce kernels of one
+        # call, each timed by its own kernel-recorded event pair, summed
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                     "traffic": traffic, "kernel": "paged_decode_partition",
+                     "traffic": traffic, "kernel": "paged_decode (plan + partition + reduce)",
                      "algorithmic_bytes_per_launch": kv_bytes,
-                     "timing": "a HIP event pair per launch on the library's stream, recorded by the kernel's own "
-                               "start and end (hipExtLaunchKernel), over a second pass of the same K steps"},
+                     "timing": "a HIP event pair per kernel on the library's stream, recorded by the kernel's own "
+                               "start and end (hipExtLaunchKernel), over a second pass of the same K steps; the "
+                               "call's kernels summed"},
+        # the partition kernel alone (the one that streams the K/V bytes)
+        "partition_kernel": {"kernel": "paged_decode_partition", "avg_us": part_us,
+                             "achieved": round(part_gbs, 2) if part_gbs else None,
+                             "frac": round(part_gbs / HBM_PEAK_GBS, 4) if part_gbs else None,
+                             "traffic": traffic},
         "kernel_hash": kernel_hash(),
     }
     pool.close()
-    result["copy_probe_GBps"] = round(copy_probe_gbs(), 1)
-    log(f"[bench] plain copy kernel: {result['copy_probe_GBps']} GB/s (read + write)")
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
-    else:
-        result["cpu_baseline"] = None
-    print(json.dumps(result), flush=True)
+    return result
 
 
 if __name__ == "__main__":
