@@ -329,6 +329,31 @@ int paged_decode(kv_pool_t* pool, const void* q, int32_t q_dtype, int32_t B, int
                  const int32_t* context_lens, int32_t max_context_len, float scale,
                  void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_decode without a workspace argument, for callers that cannot allocate
+ * device memory around the call: code under HIP graph capture, tight serving
+ * loops, and harnesses that forbid hipMalloc.  Same arguments, kernels,
+ * results (bit for bit) and errors as paged_decode, except that the work list
+ * and partial results go to a fixed scratch array the library holds in each
+ * device's memory until the process ends (PKV_NOALLOC_SCRATCH_BYTES per
+ * device).  The call allocates nothing: no hipMalloc, hipFree or allocating
+ * library routine.  It must be made with the pool's device current.
+ *   Limit: paged_decode_workspace_bytes(pool, B, H_q, max_context_len) must
+ *   not exceed PKV_NOALLOC_SCRATCH_BYTES (32 MiB: for example 64 sequences of
+ *   up to 8192 tokens with 32 query heads of 128 dims need 17 MB); larger
+ *   calls return PKV_ERR_OUT_OF_RANGE before anything is launched.
+ *   Every call on one device shares that device's scratch, which keeps the
+ *   last call's contents (the first kernel of a call resets what must start
+ *   at zero): calls that overlap on one device race and must be ordered, for
+ *   example on one stream.
+ * Errors: those of paged_decode; OUT_OF_RANGE (scratch too small); INVALID_ARG
+ * (the current device is not the pool's); DEVICE (the scratch's address could
+ * not be looked up). */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int paged_decode_noalloc(kv_pool_t* pool, const void* q, int32_t q_dtype, int32_t B, int32_t H_q,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t max_context_len, float scale,
+                         void* out, void* stream);
+
 /* Workspace bytes paged_decode needs for these sizes with the pool's current
  * partition setting (0 if one partition covers max_context_len). */
 size_t paged_decode_workspace_bytes(const kv_pool_t* pool, int32_t B, int32_t H_q,

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 F32, F16, BF16, FP8_E4M3, INT8_MINMAX = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_NO_BLOCKS, ERR_OUT_OF_RANGE, ERR_STATE, ERR_UNSUPPORTED, ERR_DEVICE = range(7)
 BLOCK = 16
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES of include/pagedkv.h
 
 _lib = None
 
@@ -88,6 +89,8 @@ _SIGNATURES = {
     "kv_append": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _P]),
     "paged_decode": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, ctypes.c_float,
                                     _P, _P, ctypes.c_size_t, _P]),
+    "paged_decode_noalloc": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, ctypes.c_float,
+                                            _P, _P]),
     "paged_decode_workspace_bytes": (ctypes.c_size_t, [_P, _I32, _I32, _I32]),
     "kv_seq_swap_bytes": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "kv_seq_swap_out": (ctypes.c_int, [_P, _I32, _P, ctypes.c_size_t, _P]),
@@ -379,6 +382,28 @@ class KVPool:
                "paged_decode")
         return out
 
+    def decode_noalloc(self, q, block_tables, context_lens, max_context_len: int, scale: float, out=None,
+                       stream=None):
+        """paged_decode_noalloc: as decode(), with the library's fixed device
+        scratch instead of a workspace (the call itself allocates nothing; an
+        `out` of None is allocated here, before the call)."""
+        torch = _torch()
+        B, H_q, D = (int(x) for x in q.shape)
+        if D != self.head_dim:
+            raise ValueError("q head_dim does not match the pool")
+        if out is None:
+            out = torch.empty_like(q)
+        qp = _dev(q, "q")
+        op = _dev(out, "out", dtype=q.dtype, shape=q.shape)
+        tp = _dev(block_tables, "block_tables", torch.int32)
+        if block_tables.dim() != 2 or block_tables.shape[0] != B:
+            raise ValueError("block_tables must be [B][max_blocks_per_seq]")
+        lp = _dev(context_lens, "context_lens", torch.int32, shape=(B,))
+        _check(lib().paged_decode_noalloc(self.handle, qp, dtype_code(q), B, H_q, tp, int(block_tables.shape[1]), lp,
+                                          int(max_context_len), float(scale), op, _stream(stream)),
+               "paged_decode_noalloc")
+        return out
+
     def swap_bytes(self, seq: int) -> int:
         n = ctypes.c_size_t()
         _check(lib().kv_seq_swap_bytes(self.handle, seq, ctypes.byref(n)), "kv_seq_swap_bytes")
@@ -468,3 +493,8 @@ def kv_append(pool: KVPool, slot_mapping, k_new, v_new, stream=None):
 def paged_decode(pool: KVPool, q, block_tables, context_lens, max_context_len, scale, out=None,
                  workspace=None, stream=None):
     return pool.decode(q, block_tables, context_lens, max_context_len, scale, out, workspace, stream)
+
+
+def paged_decode_noalloc(pool: KVPool, q, block_tables, context_lens, max_context_len, scale, out=None,
+                         stream=None):
+    return pool.decode_noalloc(q, block_tables, context_lens, max_context_len, scale, out, stream)

@@ -31,6 +31,12 @@
 #include <type_traits>
 #include <unordered_map>
 
+// Fixed scratch of paged_decode_noalloc (work list and partial results), one
+// copy per device for the life of the process.  Host code never passes this
+// name to a kernel or a copy: it only stands in for the device array on the
+// host side.  noalloc_scratch() below looks up the device address.
+static __device__ __align__(256) unsigned char scratch[pkv::kNoAllocScratchBytes];
+
 namespace pkv {
 namespace {
 
@@ -1162,6 +1168,27 @@ int resident_workgroups(KernelFn fn) {
 int decode_resident_workgroups(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G) {
     KernelFn fn = pick_partition(kv_dt, q_dt, D, decode_heads_per_wg(G));
     return fn ? resident_workgroups(fn) : 0;
+}
+
+hipError_t noalloc_scratch(int device, void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};       // per device, filled on first use (no host allocation)
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device) return hipErrorInvalidDevice;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[device] = p;
+    }
+    *ptr = addr[device];
+    return hipSuccess;
 }
 
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream) {

@@ -129,6 +129,10 @@ int decode_resident_workgroups(int32_t kv_dt, int32_t q_dt, int32_t D, int32_t G
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_partition(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
+// Device address of the fixed decode scratch on `device` (which must be the
+// current device), looked up once per device and kept; kNoAllocScratchBytes long.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(int device, void** ptr);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 hipError_t launch_move_blocks(const MoveParams& p, hipStream_t stream);

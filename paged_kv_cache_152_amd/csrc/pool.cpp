@@ -30,6 +30,8 @@
 #pragma GCC visibility pop
 #include "internal.h"
 
+static_assert(PKV_NOALLOC_SCRATCH_BYTES == pkv::kNoAllocScratchBytes, "scratch size differs from the header's");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -845,9 +847,15 @@ size_t paged_decode_workspace_bytes(const kv_pool_t* p, int32_t B, int32_t H_q, 
     return workspace_for(p, B, H_q, max_len, resolve_partition(p, B, H_q, max_len)).total;
 }
 
-int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_t H_q, const int32_t* block_tables,
-                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, float scale,
-                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// paged_decode and paged_decode_noalloc.  With `noalloc` the workspace
+// arguments are ignored and the library's fixed device scratch serves instead.
+int decode_impl(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_t H_q, const int32_t* block_tables,
+                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, float scale,
+                void* out, void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
     if (!p) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
     if (B < 0 || B > 65535) return fail(PKV_ERR_INVALID_ARG, "B must be in [0, 65535], got %d", B);
     if (H_q <= 0 || H_q % p->kv_heads != 0)
@@ -871,6 +879,24 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
         return fail(PKV_ERR_INVALID_ARG, "partition of %d tokens is too small for %d tokens", P, max_len);
     const WsLayout ws = workspace_for(p, B, H_q, max_len, P);
     const size_t need = ws.total;
+    if (noalloc) {
+        if (need > pkv::kNoAllocScratchBytes)
+            return fail(PKV_ERR_OUT_OF_RANGE, "these sizes need %zu bytes of scratch; the fixed scratch holds %zu",
+                        need, pkv::kNoAllocScratchBytes);
+        if (p->host_only) return fail(PKV_ERR_STATE, "host-only pool has no device memory");
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            int cur = -1;
+            hipError_t e = hipGetDevice(&cur);
+            if (e != hipSuccess) return hip_fail(e, "current device");
+            if (cur != p->device)
+                return fail(PKV_ERR_INVALID_ARG, "current device %d is not the pool's device %d", cur, p->device);
+            e = pkv::noalloc_scratch(cur, &workspace);
+            if (e != hipSuccess) return hip_fail(e, "decode scratch address");
+            workspace_bytes = pkv::kNoAllocScratchBytes;
+        }
+    }
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
     if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -926,6 +952,24 @@ int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_
         if (e != hipSuccess) return hip_fail(e, "paged_decode_reduce launch");
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_decode(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_t H_q, const int32_t* block_tables,
+                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, float scale,
+                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(p, q, q_dtype, B, H_q, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                       scale, out, workspace, workspace_bytes, stream, false);
+}
+
+int paged_decode_noalloc(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t B, int32_t H_q,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t max_context_len, float scale, void* out, void* stream) {
+    return decode_impl(p, q, q_dtype, B, H_q, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                       scale, out, nullptr, 0, stream, true);
 }
 
 int paged_prefill(kv_pool_t* p, const void* q, int32_t q_dtype, int32_t n_seqs, int32_t H_q, const int32_t* q_start,

@@ -315,6 +315,31 @@ def test_device_calls_validate_before_device_work():
     p.close()
 
 
+def test_decode_noalloc_validates_and_bounds_its_scratch():
+    """paged_decode_noalloc: the same argument checks as paged_decode; sizes whose
+    workspace exceeds the fixed scratch are refused with OUT_OF_RANGE before any
+    device work; a host-only pool then gives STATE."""
+    L = pkv.lib()
+    p = pkv.KVPool(8, 8, 128, pkv.F16, host_only=True)
+    h = p.handle
+    fake = ctypes.c_void_p(0x10000)     # never dereferenced: every call below is refused on the host
+    dec = lambda **kw: L.paged_decode_noalloc(h, kw.get("q", fake), pkv.F16, kw.get("B", 2), kw.get("H", 40),
+                                              fake, kw.get("mb", 4096), fake, kw.get("ml", 64), 0.125, fake, None)
+    assert dec(H=7) == pkv.ERR_INVALID_ARG
+    assert dec(q=None) == pkv.ERR_INVALID_ARG
+    assert dec() == pkv.ERR_STATE
+    # the mixed-traffic shape (256 sequences up to 65536 tokens, 40 query heads) needs more than the scratch
+    big = p.workspace_bytes(256, 40, 65536)
+    assert big > pkv.NOALLOC_SCRATCH_BYTES
+    assert dec(B=256, ml=65536) == pkv.ERR_OUT_OF_RANGE
+    assert "scratch" in pkv.last_error()
+    # a Llama-3-8B-shaped batch (64 sequences up to 8192 tokens, 32 query heads) fits
+    q = pkv.KVPool(8, 8, 128, pkv.BF16, host_only=True)
+    assert 0 < q.workspace_bytes(64, 32, 8192) <= pkv.NOALLOC_SCRATCH_BYTES
+    p.close()
+    q.close()
+
+
 def test_partition_heuristic_is_multiple_of_64():
     p = pkv.KVPool(8, 8, 128, pkv.BF16, host_only=True)
     for B, Hq, ml in ((1, 32, 1), (64, 32, 8192), (256, 40, 65536), (16, 8, 100), (1, 8, 0)):
