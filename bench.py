@@ -48,9 +48,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def traffic_for(workload: str, kernel: str, partition_tokens: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources at the same partition size; else None."""
+def traffic_for(workload: str, kernel: str, partition_tokens: int, key: str = "bytes_per_launch"):
+    """HBM bytes per launch (`key`: the dominant kernel's, or "call_bytes" for
+    every kernel of one library call) from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources at the same
+    partition size; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -58,7 +60,90 @@ def traffic_for(workload: str, kernel: str, partition_tokens: int):
         t = json.load(f)
     if t.get("kernel_hash") != kernel_hash(kernel) or t.get("partition_tokens") != partition_tokens:
         return None
-    return t.get("bytes_per_launch")
+    return t.get(key)
+
+
+COPY_PROBE_BYTES = 2 << 30     # copy_probe_gbs: bytes read (and written) by each pkv_copy launch
+CALL_KERNELS = {"paged_decode_partition": ["paged_decode_plan", "paged_decode_partition", "paged_decode_reduce"],
+                "paged_prefill": ["paged_prefill"]}
+
+
+def _pmc_mean_kib(run_dir: str, counter: str) -> dict:
+    """Mean value of `counter` per dispatch, per kernel name, from a rocprofv3
+    --pmc run's counter_collection CSV (values summed over a dispatch's rows)."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    sums, counts = {}, {}
+    for (name, _), v in per.items():
+        sums[name] = sums.get(name, 0.0) + v
+        counts[name] = counts.get(name, 0) + 1
+    return {name: sums[name] / counts[name] for name in sums}
+
+
+def _match(table: dict, short: str) -> float:
+    hits = [v for name, v in table.items() if short in name and (short != "paged_decode_partition" or "plan" not in name)]
+    if not hits:
+        raise SystemExit(f"no dispatches of {short} in the counter run")
+    return float(np.mean(hits))
+
+
+def traffic_summary(args) -> None:
+    """--traffic-from FETCH_DIR WRITE_DIR: turn two rocprofv3 counter runs of
+    this script on --workload (FETCH_SIZE, then WRITE_SIZE, each its own run)
+    into profiles/traffic_<kernel>_<workload>.json.  Each counter is scaled by
+    what it reads for pkv_copy in the same run (the copy probe moves
+    COPY_PROBE_BYTES each way per launch)."""
+    fetch_dir, write_dir = args.traffic_from
+    fetch, write = _pmc_mean_kib(fetch_dir, "FETCH_SIZE"), _pmc_mean_kib(write_dir, "WRITE_SIZE")
+    kib = COPY_PROBE_BYTES / 1024
+    fscale, wscale = kib / _match(fetch, "pkv_copy"), kib / _match(write, "pkv_copy")
+    prefill = args.workload.startswith("prefill")
+    kernel = "paged_prefill" if prefill else "paged_decode_partition"
+    if prefill:
+        w = wl.make_prefill(args.workload)
+        algo, P = w.kv_bytes(), 0
+    else:
+        w = wl.make(args.workload)
+        algo = w.kv_bytes_per_step()
+        import paged_kv_cache_152_amd as pkv
+        hp = pkv.KVPool(8, w.H_kv, w.D, w.kv_dtype, host_only=True)
+        if args.partition:
+            hp.set_partition(args.partition)
+        P = hp.partition_tokens(w.B, w.H_q, w.max_len())
+        hp.close()
+    per_kernel = {}
+    for k in CALL_KERNELS[kernel]:
+        try:
+            f, wr = _match(fetch, k) * 1024 * fscale, _match(write, k) * 1024 * wscale
+        except SystemExit:
+            continue                               # a kernel this call did not launch (one partition)
+        per_kernel[k] = {"fetch_bytes": round(f), "write_bytes": round(wr)}
+    main = per_kernel[kernel]
+    call = sum(v["fetch_bytes"] + v["write_bytes"] for v in per_kernel.values())
+    out = {"kernel": kernel, "workload": args.workload, "kernel_hash": kernel_hash(kernel), "partition_tokens": P,
+           "bytes_per_launch": main["fetch_bytes"] + main["write_bytes"], "call_bytes": call,
+           "per_kernel": per_kernel, "algorithmic_bytes_per_launch": algo,
+           "traffic_over_algorithmic": round((main["fetch_bytes"] + main["write_bytes"]) / algo, 5),
+           "call_traffic_over_algorithmic": round(call / algo, 5),
+           "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5),
+           "calibration": f"pkv_copy of {COPY_PROBE_BYTES >> 30} GiB in the same runs: FETCH_SIZE "
+                          f"{_match(fetch, 'pkv_copy'):.1f} KiB, WRITE_SIZE {_match(write, 'pkv_copy'):.1f} KiB per launch",
+           "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python -u bench.py "
+                        f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline --no-companion",
+                        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python -u bench.py "
+                        f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline --no-companion"]}
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{args.workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(path, json.dumps({k: out[k] for k in ("bytes_per_launch", "call_bytes", "traffic_over_algorithmic")}))
 
 
 def host_alloc_us(w: wl.Workload, reps: int = 20) -> float:
@@ -371,7 +456,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-companion", action="store_true",
                     help="mha7b: skip the gqa8b figures that are otherwise measured in the same run")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the workload's traffic summary from two rocprofv3 counter runs, then exit (no GPU)")
     args = ap.parse_args()
+    if args.traffic_from:
+        return traffic_summary(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(each GPU would own its own pool and sequences); use --gpus 1", file=sys.stderr)
@@ -467,6 +556,7 @@ def measure_decode(w: wl.Workload, args, spread: bool = True) -> dict:
     achieved = kv_bytes / (decode_us * 1e-6) / 1e9 if decode_us else None
     part_gbs = kv_bytes / (part_us * 1e-6) / 1e9 if part_us else None
     traffic = traffic_for(w.name, "paged_decode_partition", P)
+    call_traffic = traffic_for(w.name, "paged_decode_partition", P, "call_bytes")
     result = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -496,7 +586,7 @@ def measure_decode(w: wl.Workload, args, spread: bool = True) -> dict:
         # call, each timed by its own kernel-recorded event pair, summed
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                     "traffic": traffic, "kernel": "paged_decode (plan + partition + reduce)",
+                     "traffic": call_traffic, "kernel": "paged_decode (plan + partition + reduce)",
                      "algorithmic_bytes_per_launch": kv_bytes,
                      "timing": "a HIP event pair per kernel on the library's stream, recorded by the kernel's own "
                                "start and end (hipExtLaunchKernel), over a second pass of the same K steps; the "

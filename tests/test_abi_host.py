@@ -438,3 +438,43 @@ def test_prefill_validates_before_device_work():
         assert L.paged_prefill(q.handle, fake, dt, 1, 2, fake, 1, 1, fake, 1, fake, 0.1, 1, fake, None) \
             == pkv.ERR_UNSUPPORTED
         q.close()
+
+
+def test_bench_traffic_summary_from_counter_csvs(tmp_path, monkeypatch):
+    """bench.py --traffic-from: per-dispatch counter sums averaged per kernel,
+    scaled by the copy kernel's reading of its known 2 GiB, summed over the
+    decode call's kernels."""
+    import csv
+    import json
+    import bench
+    rows = {"FETCH_SIZE": [("pkv::pkv_copy_kernel(x)", 1, 1048576.0), ("pkv::pkv_copy_kernel(x)", 2, 1048576.0),
+                           ("pkv::paged_decode_plan(p)", 3, 1.0),
+                           ("void pkv::paged_decode_partition_gqa<2, 2, 4>(p)", 4, 500000.0),
+                           ("void pkv::paged_decode_partition_gqa<2, 2, 4>(p)", 5, 600000.0),
+                           ("void pkv::paged_decode_reduce<2, 128>(p)", 6, 2000.0)],
+            "WRITE_SIZE": [("pkv::pkv_copy_kernel(x)", 1, 2097152.0), ("pkv::paged_decode_plan(p)", 3, 2.0),
+                           ("void pkv::paged_decode_partition_gqa<2, 2, 4>(p)", 4, 4000.0),
+                           ("void pkv::paged_decode_reduce<2, 128>(p)", 6, 500.0)]}
+    dirs = []
+    for counter, data in rows.items():
+        d = tmp_path / counter
+        d.mkdir()
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            wr = csv.writer(f)
+            wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            for name, disp, val in data:
+                wr.writerow([disp, name, counter, val / 2])          # two rows per dispatch, summed
+                wr.writerow([disp, name, counter, val / 2])
+        dirs.append(str(d))
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_hash", lambda kernel="x": "h")
+    args = type("A", (), {"traffic_from": dirs, "workload": "gqa8b", "partition": 0})()
+    bench.traffic_summary(args)
+    t = json.load(open(prof / "traffic_paged_decode_partition_gqa8b.json"))
+    assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0
+    part = t["per_kernel"]["paged_decode_partition"]
+    assert part["fetch_bytes"] == 550000 * 1024 * 2 and part["write_bytes"] == 4000 * 1024
+    assert t["bytes_per_launch"] == part["fetch_bytes"] + part["write_bytes"]
+    assert t["call_bytes"] == (1 + 550000 + 2000) * 2048 + (2 + 4000 + 500) * 1024

@@ -235,6 +235,17 @@ def test_many_partitions_merge(dt):
     assert_close(runs[0], expected(w), dt, "many partitions")
 
 
+def test_batch_beyond_one_plan_workgroup():
+    """1100 sequences (more than the plan kernel's 1024 threads, so its loop
+    over later sequences runs), lengths over several partitions and short
+    ones: every sequence against the oracle."""
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.choice([1, 17, 64, 300, 700, 1500], size=1100)]
+    w = _small(wl.BF16, 8, 2, 128, lens, seed=78)
+    got = run_case(w, partition=256)
+    assert_close(got, expected(w), wl.BF16, "1100 sequences")
+
+
 @pytest.mark.parametrize("dt", [wl.BF16, wl.E4M3])
 def test_uniform_lengths_automatic_partition(dt):
     """Every context the same length with the automatic partition: the plan
