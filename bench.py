@@ -539,6 +539,7 @@ def measure_decode(w: wl.Workload, args, spread: bool = True) -> dict:
     torch.cuda.synchronize()
     stats = pool.profile_read()
     pool.profile_enable(False)
+    graph = graph_steps(torch, prep, out, ws, stream, args.steps, w.kv_bytes_per_step())
     step_dist = None
     if spread:
         step_dist = {m: per_step_us(torch, prep, out, ws, stream, args.steps, m) for m in ("warm", "cold", "after_write")}
@@ -597,9 +598,36 @@ def measure_decode(w: wl.Workload, args, spread: bool = True) -> dict:
                              "frac": round(part_gbs / HBM_PEAK_GBS, 4) if part_gbs else None,
                              "traffic": traffic},
         "kernel_hash": kernel_hash(),
+        "graph": graph,
     }
     pool.close()
     return result
+
+
+def graph_steps(torch, prep, out, ws, stream, n: int, kv_bytes: int):
+    """The same step captured once into a HIP graph (through torch) and replayed
+    n times between two events: the per-step figure without host launch cost.
+    Reported beside value, which stays the eagerly launched step."""
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            prep.step(out=out, workspace=ws)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        del g
+        log(f"[bench] graph replay: {ms * 1e3:.1f} us/step")
+        return {"ms_per_step": round(ms, 5), "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+                "how": "one step (kv_append + paged_decode) captured with torch.cuda.graph, replayed back to back"}
+    except Exception as e:                      # capture refused: report, do not fail the bench
+        log(f"[bench] graph capture failed: {e}")
+        return None
 
 
 if __name__ == "__main__":
