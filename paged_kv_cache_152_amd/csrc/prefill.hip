@@ -404,11 +404,13 @@ __global__ __launch_bounds__(kPfWaves * 64) void paged_prefill_kernel(PrefillPar
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit pools: K and V go from HBM straight into LDS (global_load_lds_dwordx4,
-// no registers on the way), in kStages LDS buffers of one 32-token stage (two
-// blocks) each, filled and consumed a pair of stages at a time: while a wave
-// computes stages j and j + 1, stages j + 2 and j + 3 are landing, and one
-// wait plus one barrier per pair hands the next pair over.  A stage row is one
+// 16-bit pools (and E4M3 at head_dim 128): K and V go from HBM straight into
+// LDS (global_load_lds_dwordx4, no registers on the way), in kStages LDS
+// buffers of one 32-token stage (two blocks) each: while a wave computes one
+// stage, the next three are landing, and one wait plus one barrier per stage
+// hands the next one over.  The compute is software-pipelined one stage deep
+// (S^T of stage j + 1 runs on the matrix cores while the weights of stage j
+// are taken on the vector ALUs; see the stage loop).  A stage row is one
 // token's head_dim values; its 16-byte chunks are
 // XOR-swizzled by row so that the K-operand reads (16 rows, one chunk each)
 // and the transposed V reads (4 rows x 32 bytes per 16 lanes) hit distinct
@@ -449,23 +451,9 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-// Max across the four lanes of a row (l % 16 equal): v_permlane16_swap pairs
-// row r with row r ^ 1 (lanes 16 apart), v_permlane32_swap pairs r with r ^ 2.
-// After a swap of a value with itself, the two results hold, in every lane,
-// that lane's value and its partner's (16 or 32 lanes away), so their max is
-// the pair's max and the value itself need not be kept alive for it (one
-// register copy per swap instead of two).
-__device__ __forceinline__ float row_max4(float v) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, v);
-    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const float m = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)a[0]),
-                                                  __builtin_bit_cast(float, (uint32_t)a[1]));
-    const uint32_t w = __builtin_bit_cast(uint32_t, m);
-    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
-}
-
-// row_max4 of two values a, b at once.  A 32-lane swap of a against b leaves
+// Max across the four lanes of a row (l % 16 equal; v_permlane16_swap pairs
+// row r with row r ^ 1, v_permlane32_swap r with r ^ 2) of two values a, b at
+// once.  A 32-lane swap of a against b leaves
 // a's lanes 0-31 and b's lanes 0-31 in the first result and both upper halves
 // in the second, so their max holds a's pair max (lanes l, l + 32) in lanes
 // 0-31 and b's in lanes 32-63; a 16-lane swap of that with itself completes
@@ -569,6 +557,32 @@ __device__ __forceinline__ int32_t scalar_read(const int32_t* ptr) {
     asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
     return v;
 }
+// Two such reads under one wait.
+__device__ __forceinline__ void scalar_read2(const int32_t* a, const int32_t* b, int32_t& x, int32_t& y) {
+    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(x), "=&s"(y)
+                 : "s"(a), "s"(b)
+                 : "memory");
+}
+
+// Direct-to-LDS loads of 16 bytes a lane (global_load_lds_dwordx4: lane l's
+// bytes land at LDS byte M0 + 16 l), written as asm.  From the builtin, the
+// compiler tracks these loads and, unable to tell which LDS bytes they write,
+// makes every later LDS read wait until all of them have landed, which would
+// drain the stage ring at every step; the stage loop does its own waiting (a
+// vector-memory count, then a barrier, before a stage is read).  The
+// instruction writes no register.  An M0 write needs one wait state before
+// the load reads it.
+// M0 is named as clobbered; these kernels make no other use of it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds) : "m0");
+}
+__device__ __forceinline__ void lds_dma16(const char* vaddr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(vaddr), "s"(lds) : "m0");
+}
+#pragma clang diagnostic pop
 
 template <int KDT, int QDT, int D>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill_dma_kernel(PrefillParams p) {
@@ -588,7 +602,6 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     static_assert(F8 ? QDT != KDT : QDT == KDT, "16-bit pools take queries of their own type");
     using QV = typename Vec8<QDT>::T;
     using PV = typename Vec8<PT>::T;
-    typedef __attribute__((address_space(3))) void lds_void;
     __shared__ __align__(16) unsigned char k_lds[kStages][SB];
     __shared__ __align__(16) unsigned char v_lds[kStages][SB];
 
@@ -656,92 +669,127 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (int64_t)g * kBlock * ROWB;
     const char* zero = reinterpret_cast<const char*>(p.zero_tile);
     const int64_t blk_stride = (int64_t)p.H_kv * kBlock * ROWB;
-    int ld_row[NI], ld_off[NI];
+    int ld_off[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int slot = (wave * NI + i) * 64 + lane;
         const int row = slot / CH, pch = slot % CH;
-        ld_row[i] = row;
         ld_off[i] = (row % kBlock) * ROWB + ((pch ^ chunk_swizzle<SWZ>(row)) * 16);
     }
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    auto issue = [&](int jj) {                 // the loads of stage jj (blocks 2 jj, 2 jj + 1)
+    auto lds_addr = [](const unsigned char* ptr) {     // LDS byte address of a shared-memory pointer
+        return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)ptr;
+    };
+    // The loads of stage jj (blocks 2 jj, 2 jj + 1) into buffer BUF = jj % 4.
+    auto issue = [&](int jj, auto BUF) {
         // wave-uniform table reads: scalar loads, which do not count against the
         // vector-memory counter the stage waits use
-        const int ph0 = scalar_read(table + 2 * jj);
-        const int ph1 = 2 * jj + 1 < nblk ? scalar_read(table + 2 * jj + 1) : -1;
+        // Stages past the last one (jj >= n_it) keep the ring's waits uniform:
+        // they have no blocks and read the zero tile.
+        int ph0 = -1, ph1 = -1;
+        if (2 * jj + 1 < nblk) scalar_read2(table + 2 * jj, table + 2 * jj + 1, ph0, ph1);
+        else if (2 * jj < nblk) ph0 = scalar_read(table + 2 * jj);
         const bool ok0 = ph0 >= 0 && ph0 < p.num_blocks, ok1 = ph1 >= 0 && ph1 < p.num_blocks;
         const bool full = ok0 && ok1 && (2 * jj + 2) * kBlock <= n;          // uniform
-        const int buf = jj % kStages;
+        constexpr int buf = decltype(BUF)::value;
+        if (full) {                            // uniform base + 32-bit lane offset
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int h = ((wave_u * NI + i) * (64 / CH)) / kBlock;          // uniform: block of this load
-            const int ph = h ? ph1 : ph0;
-            const int dst = (wave_u * NI + i) * 64 * 16;                      // bytes
-            const char* ks;
-            const char* vs;
-            if (full) {                        // uniform base + 32-bit lane offset
-                ks = kbase + (int64_t)ph * blk_stride + (uint32_t)ld_off[i];
-                vs = vbase + (int64_t)ph * blk_stride + (uint32_t)ld_off[i];
-            } else {
-                const bool ok = (h ? ok1 : ok0) && 2 * jj * kBlock + ld_row[i] < n;
-                ks = ok ? kbase + (int64_t)ph * blk_stride + ld_off[i] : zero + ld_off[i];
-                vs = ok ? vbase + (int64_t)ph * blk_stride + ld_off[i] : zero + ld_off[i];
+            for (int i = 0; i < NI; ++i) {
+                const int h = ((wave_u * NI + i) * (64 / CH)) / kBlock;      // uniform: block of this load
+                const int64_t base = (int64_t)(uint32_t)(h ? ph1 : ph0) * blk_stride;   // ph checked >= 0
+                const int dst = (wave_u * NI + i) * 64 * 16;                  // bytes
+                // a scalar base plus the lane's 32-bit offset
+                lds_dma16(kbase + base, (uint32_t)ld_off[i], lds_addr(&k_lds[buf][dst]));
+                lds_dma16(vbase + base, (uint32_t)ld_off[i], lds_addr(&v_lds[buf][dst]));
             }
-            __builtin_amdgcn_global_load_lds(ks, (lds_void*)&k_lds[buf][dst], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vs, (lds_void*)&v_lds[buf][dst], 16, 0, 0);
+        } else {                               // rows past the context or in a bad block read the zero tile
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int h = ((wave_u * NI + i) * (64 / CH)) / kBlock;
+                const int ph = h ? ph1 : ph0;
+                const int dst = (wave_u * NI + i) * 64 * 16;
+                // formed here, not hoisted out of the loop as 64-bit registers
+                uint32_t off = (uint32_t)ld_off[i];
+                int ln = lane;
+                asm volatile("" : "+v"(off), "+v"(ln));
+                const int ld_row = ((wave_u * NI + i) * 64 + ln) / CH;      // stage row of this lane's chunk
+                const bool ok = (h ? ok1 : ok0) && 2 * jj * kBlock + ld_row < n;
+                const char* ks = ok ? kbase + (int64_t)ph * blk_stride + off : zero + off;
+                const char* vs = ok ? vbase + (int64_t)ph * blk_stride + off : zero + off;
+                lds_dma16(ks, lds_addr(&k_lds[buf][dst]));
+                lds_dma16(vs, lds_addr(&v_lds[buf][dst]));
+            }
         }
     };
 
     f32x4_t acc[R][MT];
-    // m_run is the reference max; neg_m (its negation, 0 while it is -inf) and
-    // thr (the level a block max must pass to move it) change only with it.
-    float m_run[R], l_run[R], neg_m[R], thr[R];
+    // m_run is the reference max, finite from the start: a row's first block
+    // with a visible token moves it (its weights before that are exp2(-inf) = 0,
+    // and the rescale factor exp2(kNoMax - m) is 0).
+    constexpr float kNoMax = -1e30f;
+    float m_run[R], l_run[R];
 #pragma unroll
     for (int rg = 0; rg < R; ++rg) {
-        m_run[rg] = -INFINITY;
-        neg_m[rg] = 0.0f;
-        thr[rg] = -INFINITY + kLazy;
+        m_run[rg] = kNoMax;
         l_run[rg] = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
     const int wg_min_see = p.causal ? n - q_len + tile0 : n - 1;
-    auto compute = [&](bool masked, int j, auto BUF) {
+    // Stage jj needs masking if it reaches past the context or past the diagonal
+    // of the workgroup's first query token.
+    auto stage_masked = [&](int jj) {
+        const int t0 = 2 * jj * kBlock;
+        return !(t0 + 2 * kBlock <= n && t0 + 2 * kBlock - 1 <= wg_min_see);
+    };
+
+    // S^T of the stage in buffer BUF for both row groups: lane (r, c) gets the
+    // logits of tokens 4 r .. +3 of block 0 (z[rg][0..3]) and of block 1
+    // (z[rg][4..7]) for row c.  The K operand of block h (token c, dims 32 k +
+    // 8 r .. +7: 16 bytes, or 8 E4M3 codes widened exactly to q's type) is read
+    // from LDS one block at a time.
+    auto s_mma = [&](auto BUF, float (&z)[R][8]) {
         constexpr int buf = decltype(BUF)::value;
         const unsigned char* kt = k_lds[buf];
-        const unsigned char* vt = v_lds[0];        // V reads: buffer 0's address + buf * SB as an immediate
-        // K operand of block h: token c, dims 32 k + 8 r .. +7 (16 bytes, or 8
-        // E4M3 codes widened exactly to q's type)
-        QV ka[2][KS];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int row = h * kBlock + c;
+            QV ka[KS];
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
                 if constexpr (F8)
-                    ka[h][k] = __builtin_bit_cast(QV, fp8x8_to<QDT>(*reinterpret_cast<const uint2*>(
+                    ka[k] = __builtin_bit_cast(QV, fp8x8_to<QDT>(*reinterpret_cast<const uint2*>(
                         kt + row * ROWB + ((2 * k + (r >> 1)) ^ chunk_swizzle<SWZ>(row)) * 16 + (r & 1) * 8)));
                 else
-                    ka[h][k] = *reinterpret_cast<const QV*>(kt + row * ROWB + ((4 * k + r) ^ chunk_swizzle<SWZ>(row)) * 16);
+                    ka[k] = *reinterpret_cast<const QV*>(kt + row * ROWB + ((4 * k + r) ^ chunk_swizzle<SWZ>(row)) * 16);
+            }
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg) {
+                f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int k = 0; k < KS; ++k) S = mma_k32<QDT>(ka[k], qb[rg][k], S);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) z[rg][4 * h + i] = S[i];
             }
         }
-        // V^T operand, dims 16 mt + c, tokens 4 r .. +3 of block 0 then of block 1,
-        // read now so that its LDS latency overlaps the K reads' (375 instead of
-        // 382 us on a 16 x (2048 + 512)-token causal chunk workload).
-        // ds_read_b64_tr_b16 builds, in each 16-lane group, row k from the 4
-        // elements lanes 4k .. 4k + 3 point at and hands lane i element i of rows
-        // 0 .. 3; so lane (r, c) points at token 4 r + c / 4, dims 16 mt + 4 (c % 4).
-        // Block 1's rows sit 16 rows (16 * ROWB bytes) after block 0's, with the same swizzle.
-        // E4M3 pools: ds_read_b64_tr_b8 builds, in each 16-lane group, row k
-        // from the 16 bytes lanes 2k, 2k + 1 point at and hands lane i byte i
-        // of rows 0 .. 7.  Lane (r, c) points at the token that k-index
-        // 8 r + c / 2 stands for (tokens 4 r .. +3 of block 0, then of block
-        // 1), dims 16 mt + 8 (c % 2) .. +7, so one read per m-tile gives the
-        // lane its 8 codes of dim 16 mt + c, widened exactly to f16.
-        constexpr int NV = F8 ? MT / 8 : MT / 4;          // issue groups of 8 reads
-        u32x2_t vh[NV][8];
+    };
+    // V^T operand of the stage in buffer BUF, dims 16 mt + c, tokens 4 r .. +3 of
+    // block 0 then of block 1.
+    // ds_read_b64_tr_b16 builds, in each 16-lane group, row k from the 4
+    // elements lanes 4k .. 4k + 3 point at and hands lane i element i of rows
+    // 0 .. 3; so lane (r, c) points at token 4 r + c / 4, dims 16 mt + 4 (c % 4).
+    // Block 1's rows sit 16 rows (16 * ROWB bytes) after block 0's, with the same swizzle.
+    // E4M3 pools: ds_read_b64_tr_b8 builds, in each 16-lane group, row k
+    // from the 16 bytes lanes 2k, 2k + 1 point at and hands lane i byte i
+    // of rows 0 .. 7.  Lane (r, c) points at the token that k-index
+    // 8 r + c / 2 stands for (tokens 4 r .. +3 of block 0, then of block
+    // 1), dims 16 mt + 8 (c % 2) .. +7, so one read per m-tile gives the
+    // lane its 8 codes of dim 16 mt + c, widened exactly to f16.
+    constexpr int NV = F8 ? MT / 8 : MT / 4;          // issue groups of 8 reads
+    auto v_issue = [&](auto BUF, u32x2_t (&vh)[NV][8]) {
+        constexpr int buf = decltype(BUF)::value;
+        const unsigned char* vt = v_lds[0];        // buffer 0's address + buf * SB as an immediate
         if constexpr (F8) {
             const int kk = c >> 1;
             const int trow = kk < 4 ? 4 * r + kk : kBlock + 4 * r + (kk - 4);
@@ -770,23 +818,16 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
                 tr_issue8<buf * SB, kBlock * ROWB>(a[0], a[1], a[2], a[3], vh[m4 / 4]);
             }
         }
-        const int tok = 2 * j * kBlock + 4 * r;
-        PV pb[R];
-        float z[R][8], mx[R];
+    };
+    auto v_wait = [&](u32x2_t (&vh)[NV][8]) {
 #pragma unroll
-        for (int rg = 0; rg < R; ++rg) {
-            f32x4_t S0 = {0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                S0 = mma_k32<QDT>(ka[0][k], qb[rg][k], S0);
-                S1 = mma_k32<QDT>(ka[1][k], qb[rg][k], S1);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                z[rg][i] = S0[i];
-                z[rg][4 + i] = S1[i];
-            }
-        }
+        for (int v = 0; v < NV; ++v) tr_wait8(vh[v]);
+    };
+    // Mask the logits of stage jj, take the block max of each row and, where it
+    // passes the row's threshold, move the reference max and rescale the row's
+    // sum and accumulators.
+    auto row_update = [&](bool masked, int jj, float (&z)[R][8]) {
+        const int tok = 2 * jj * kBlock + 4 * r;
         if (masked) {                          // one uniform branch for both row groups
 #pragma unroll
             for (int rg = 0; rg < R; ++rg) {
@@ -797,41 +838,58 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
                     z[rg][i] = (i >> 2) * kBlock + (i & 3) <= lim ? z[rg][i] : -INFINITY;   // select, never 0 * garbage
             }
         }
-#pragma unroll
-        for (int rg = 0; rg < R; ++rg)
-            mx[rg] = vmax3(vmax3(z[rg][0], z[rg][1], z[rg][2]), vmax3(z[rg][3], z[rg][4], z[rg][5]),
-                           vmax3(z[rg][6], z[rg][7], z[rg][7]));
-        static_assert(R == 2, "row maxes are reduced in pairs");
-        float rmax[R];
-        row_max4x2(mx[0], mx[1], rmax[0], rmax[1]);
+        // Lazy reference max: a row's reference moves only when a logit passes
+        // it by more than kLazy (weights up to 2^kLazy are fine in every P
+        // type).  Each lane tests its own 8 logits; only when some lane of the
+        // wave passes is the row max taken across the row's 4 lanes.
+        float mx[R];
+        bool pass = false;
 #pragma unroll
         for (int rg = 0; rg < R; ++rg) {
-            const float m_blk = rmax[rg] * qscale;
-            if (__builtin_amdgcn_ballot_w64(m_blk > thr[rg]) != 0) {
-                const float m_new = m_blk > thr[rg] ? m_blk : m_run[rg];
-                const float alpha = m_new == m_run[rg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
-                l_run[rg] *= alpha;
+            mx[rg] = vmax3(vmax3(z[rg][0], z[rg][1], z[rg][2]), vmax3(z[rg][3], z[rg][4], z[rg][5]),
+                           __builtin_elementwise_maximum(z[rg][6], z[rg][7]));
+            pass = pass || mx[rg] * qscale - m_run[rg] > kLazy;
+        }
+        if (__builtin_amdgcn_ballot_w64(pass) != 0) {
+            static_assert(R == 2, "row maxes are reduced in pairs");
+            float rmax[R];
+            row_max4x2(mx[0], mx[1], rmax[0], rmax[1]);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[rg][mt] *= alpha;
-                m_run[rg] = m_new;
-                neg_m[rg] = m_new == -INFINITY ? 0.0f : -m_new;
-                thr[rg] = m_new + kLazy;
+            for (int rg = 0; rg < R; ++rg) {
+                const float m_blk = rmax[rg] * qscale;
+                const bool moves = m_blk - m_run[rg] > kLazy;
+                if (__builtin_amdgcn_ballot_w64(moves) != 0) {
+                    const float m_new = moves ? m_blk : m_run[rg];
+                    const float alpha = m_new == m_run[rg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
+                    l_run[rg] *= alpha;
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[rg][mt] *= alpha;
+                    m_run[rg] = m_new;
+                }
             }
+        }
+    };
+    // P = exp2(z * qscale - m) in P.V's 16-bit type.  l sums the rounded weights
+    // P.V multiplies (a normalised average of them); each lane keeps the part of
+    // its own tokens, all four lanes of a row rescale alike, and the parts are
+    // added at the end.
+    auto softmax = [&](const float (&z)[R][8], PV (&pb)[R]) {
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) {
             float pr[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(z[rg][i], qscale, neg_m[rg]));
-            // l sums the rounded weights P.V multiplies (a normalised average of
-            // them); each lane keeps the part of its own tokens, all four lanes of
-            // a row rescale alike, and the parts are added at the end
+            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(z[rg][i], qscale, -m_run[rg]));
             const uint4 pw = make_uint4(pack2<PT>(pr[0], pr[1]), pack2<PT>(pr[2], pr[3]),
                                         pack2<PT>(pr[4], pr[5]), pack2<PT>(pr[6], pr[7]));
             l_run[rg] = add_pair<PT>(pw.w, add_pair<PT>(pw.z, add_pair<PT>(pw.y, add_pair<PT>(pw.x, l_run[rg]))));
             pb[rg] = __builtin_bit_cast(PV, pw);
         }
+    };
+    // O^T += V^T . P^T over the stage's 32 tokens.
+    auto pv_mma = [&](const u32x2_t (&vh)[NV][8], const PV (&pb)[R]) {
         if constexpr (F8) {
 #pragma unroll
             for (int m8 = 0; m8 < MT; m8 += 8) {
-                tr_wait8(vh[m8 / 8]);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const PV va = __builtin_bit_cast(PV, fp8x8_to<DT_F16>(make_uint2(vh[m8 / 8][u].x, vh[m8 / 8][u].y)));
@@ -842,10 +900,10 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         } else {
 #pragma unroll
             for (int m4 = 0; m4 < MT; m4 += 4) {
-                tr_wait8(vh[m4 / 4]);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const PV va = __builtin_bit_cast(PV, make_uint4(vh[m4 / 4][2 * u].x, vh[m4 / 4][2 * u].y, vh[m4 / 4][2 * u + 1].x, vh[m4 / 4][2 * u + 1].y));
+                    const PV va = __builtin_bit_cast(PV, make_uint4(vh[m4 / 4][2 * u].x, vh[m4 / 4][2 * u].y,
+                                                                     vh[m4 / 4][2 * u + 1].x, vh[m4 / 4][2 * u + 1].y));
 #pragma unroll
                     for (int rg = 0; rg < R; ++rg) acc[rg][m4 + u] = mma_k32<PT>(va, pb[rg], acc[rg][m4 + u]);
                 }
@@ -853,30 +911,65 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         }
     };
 
-    // Stages go in pairs: one wait and one barrier per pair (half the barriers
-    // of one per stage: 394 -> 386 us on a 16 x (2048 + 512)-token causal
-    // chunk workload).  The pair j, j + 1 was issued two stages earlier; once
-    // it has landed, the barrier also means every wave is done with the
-    // previous pair's buffers, which the next pair then refills.
-    // The loop is unrolled over the four buffers, so that each stage's LDS
-    // addresses are loop-invariant registers plus immediate offsets.
-    static_assert(kStages == 4, "two pairs of stage buffers");
+    // Software pipeline over stages of two blocks.  Step j turns the logits of
+    // stage j (already masked, with the row maxes applied) into weights and
+    // accumulates P.V of stage j, while it computes the logits of stage j + 1:
+    // the matrix cores work on S^T(j + 1) while the vector ALUs take the
+    // exponentials of stage j, and on P.V(j) while they take the maxes of
+    // stage j + 1, so the two units overlap within one wave.
+    //
+    // Buffers.  Stage s lives in buffer s % 4.  Its K is read in step s - 1
+    // before S^T(s), its V at the end of step s - 1, and both reads are
+    // complete before step s begins.  Step j waits until stage j + 1 has
+    // landed, meets the other waves (after which no wave reads stage j's
+    // buffer), and refills that buffer with stage j + 4: three stages are in
+    // flight while one is computed.  Stages past the end are issued too (from
+    // the zero tile), so that every wait counts the same loads; they are
+    // drained before the workgroup ends.
+    constexpr int LPS = 2 * NI;                // loads per stage per wave
+    float z[R][8];
+    u32x2_t vh[NV][8];
+    if (n_it > 0) {
+        issue(0, StageBuf<0>{});
+        issue(1, StageBuf<1>{});
+        issue(2, StageBuf<2>{});
+        issue(3, StageBuf<3>{});
+        wait_loads_then_barrier<(kStages - 1) * LPS>();
+        s_mma(StageBuf<0>{}, z);
+        row_update(stage_masked(0), 0, z);
+        v_issue(StageBuf<0>{}, vh);
+        v_wait(vh);
+    }
+    static_assert(kStages == 4, "the loop is unrolled over four buffers");
+    // Step j < n_it - 1 (the last stage's P.V follows the loop).
     auto step = [&](int j, auto BUF) {
-        if constexpr (decltype(BUF)::value % 2 == 0) {
-            wait_loads_then_barrier<0>();
-            if (j + 2 < n_it) issue(j + 2);
-            if (j + 3 < n_it) issue(j + 3);
-        }
-        const int t0 = 2 * j * kBlock;
-        compute(!(t0 + 2 * kBlock <= n && t0 + 2 * kBlock - 1 <= wg_min_see), j, BUF);
+        constexpr int nbuf = (decltype(BUF)::value + 1) % kStages;
+        wait_loads_then_barrier<2 * LPS>();
+        issue(j + 4, BUF);                     // (j + 4) % 4 == j % 4
+        PV pb[R];
+        softmax(z, pb);
+        float zn[R][8];
+        s_mma(StageBuf<nbuf>{}, zn);
+        pv_mma(vh, pb);
+        row_update(stage_masked(j + 1), j + 1, zn);
+        v_issue(StageBuf<nbuf>{}, vh);
+        v_wait(vh);
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) z[rg][i] = zn[rg][i];
     };
-    if (n_it > 0) issue(0);
-    if (n_it > 1) issue(1);
-    for (int j = 0; j < n_it; j += kStages) {
+    for (int j = 0; j < n_it - 1; j += kStages) {
         step(j, StageBuf<0>{});
-        if (j + 1 < n_it) step(j + 1, StageBuf<1>{});
-        if (j + 2 < n_it) step(j + 2, StageBuf<2>{});
-        if (j + 3 < n_it) step(j + 3, StageBuf<3>{});
+        if (j + 1 < n_it - 1) step(j + 1, StageBuf<1>{});
+        if (j + 2 < n_it - 1) step(j + 2, StageBuf<2>{});
+        if (j + 3 < n_it - 1) step(j + 3, StageBuf<3>{});
+    }
+    if (n_it > 0) {
+        PV pb[R];
+        softmax(z, pb);
+        pv_mma(vh, pb);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stages past the end
     }
 
     uint16_t* o16 = reinterpret_cast<uint16_t*>(p.out);
