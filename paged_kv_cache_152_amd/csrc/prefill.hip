@@ -744,31 +744,34 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         return !(t0 + 2 * kBlock <= n && t0 + 2 * kBlock - 1 <= wg_min_see);
     };
 
-    // S^T of the stage in buffer BUF for both row groups: lane (r, c) gets the
-    // logits of tokens 4 r .. +3 of block 0 (z[rg][0..3]) and of block 1
-    // (z[rg][4..7]) for row c.  The K operand of block h (token c, dims 32 k +
-    // 8 r .. +7: 16 bytes, or 8 E4M3 codes widened exactly to q's type) is read
-    // from LDS one block at a time.
-    auto s_mma = [&](auto BUF, float (&z)[R][8]) {
+    // K operand of the stage in buffer BUF, block h: token c, dims 32 k + 8 r ..
+    // +7 (16 bytes, or 8 E4M3 codes widened exactly to q's type).
+    auto k_read = [&](auto BUF, QV (&ka)[2][KS]) {
         constexpr int buf = decltype(BUF)::value;
         const unsigned char* kt = k_lds[buf];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int row = h * kBlock + c;
-            QV ka[KS];
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
                 if constexpr (F8)
-                    ka[k] = __builtin_bit_cast(QV, fp8x8_to<QDT>(*reinterpret_cast<const uint2*>(
+                    ka[h][k] = __builtin_bit_cast(QV, fp8x8_to<QDT>(*reinterpret_cast<const uint2*>(
                         kt + row * ROWB + ((2 * k + (r >> 1)) ^ chunk_swizzle<SWZ>(row)) * 16 + (r & 1) * 8)));
                 else
-                    ka[k] = *reinterpret_cast<const QV*>(kt + row * ROWB + ((4 * k + r) ^ chunk_swizzle<SWZ>(row)) * 16);
+                    ka[h][k] = *reinterpret_cast<const QV*>(kt + row * ROWB + ((4 * k + r) ^ chunk_swizzle<SWZ>(row)) * 16);
             }
+        }
+    };
+    // S^T of both blocks for both row groups: lane (r, c) gets the logits of
+    // tokens 4 r .. +3 of block 0 (z[rg][0..3]) and of block 1 (z[rg][4..7]) for row c.
+    auto s_mma = [&](const QV (&ka)[2][KS], float (&z)[R][8]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
             for (int rg = 0; rg < R; ++rg) {
                 f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int k = 0; k < KS; ++k) S = mma_k32<QDT>(ka[k], qb[rg][k], S);
+                for (int k = 0; k < KS; ++k) S = mma_k32<QDT>(ka[h][k], qb[rg][k], S);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) z[rg][4 * h + i] = S[i];
             }
@@ -823,10 +826,10 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
         for (int v = 0; v < NV; ++v) tr_wait8(vh[v]);
     };
-    // Mask the logits of stage jj, take the block max of each row and, where it
-    // passes the row's threshold, move the reference max and rescale the row's
-    // sum and accumulators.
-    auto row_update = [&](bool masked, int jj, float (&z)[R][8]) {
+    // Mask the logits of stage jj (mask), then take the block max of each row
+    // and, where it passes the row's threshold, move the reference max and
+    // rescale the row's sum and accumulators (row_update).
+    auto mask = [&](bool masked, int jj, float (&z)[R][8]) {
         const int tok = 2 * jj * kBlock + 4 * r;
         if (masked) {                          // one uniform branch for both row groups
 #pragma unroll
@@ -838,6 +841,8 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
                     z[rg][i] = (i >> 2) * kBlock + (i & 3) <= lim ? z[rg][i] : -INFINITY;   // select, never 0 * garbage
             }
         }
+    };
+    auto row_update = [&](float (&z)[R][8]) {
         // Lazy reference max: a row's reference moves only when a logit passes
         // it by more than kLazy (weights up to 2^kLazy are fine in every P
         // type).  Each lane tests its own 8 logits; only when some lane of the
@@ -935,8 +940,11 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         issue(2, StageBuf<2>{});
         issue(3, StageBuf<3>{});
         wait_loads_then_barrier<(kStages - 1) * LPS>();
-        s_mma(StageBuf<0>{}, z);
-        row_update(stage_masked(0), 0, z);
+        QV ka[2][KS];
+        k_read(StageBuf<0>{}, ka);
+        s_mma(ka, z);
+        mask(stage_masked(0), 0, z);
+        row_update(z);
         v_issue(StageBuf<0>{}, vh);
         v_wait(vh);
     }
@@ -946,13 +954,20 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         constexpr int nbuf = (decltype(BUF)::value + 1) % kStages;
         wait_loads_then_barrier<2 * LPS>();
         issue(j + 4, BUF);                     // (j + 4) % 4 == j % 4
+        QV ka[2][KS];
+        k_read(StageBuf<nbuf>{}, ka);
         PV pb[R];
         softmax(z, pb);
+        // the weights are formed here, beside S^T(j + 1) on the matrix cores,
+        // not sunk past the mask branch to where P.V uses them
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) asm volatile("" ::"v"(pb[rg]));
         float zn[R][8];
-        s_mma(StageBuf<nbuf>{}, zn);
+        s_mma(ka, zn);
+        mask(stage_masked(j + 1), j + 1, zn);  // before P.V(j), so that P.V and the maxes share a block
         pv_mma(vh, pb);
-        row_update(stage_masked(j + 1), j + 1, zn);
-        v_issue(StageBuf<nbuf>{}, vh);
+        v_issue(StageBuf<nbuf>{}, vh);         // the registers P.V(j) has just read
+        row_update(zn);
         v_wait(vh);
 #pragma unroll
         for (int rg = 0; rg < R; ++rg)
