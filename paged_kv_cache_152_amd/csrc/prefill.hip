@@ -473,27 +473,6 @@ __device__ __forceinline__ void row_max4x2(float a, float b, float& ma, float& m
     mb = __builtin_bit_cast(float, (uint32_t)u[1]);
 }
 
-__device__ __forceinline__ float row_sum4(float v) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, v);
-    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const float s = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
-    const uint32_t w = __builtin_bit_cast(uint32_t, s);
-    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
-}
-
-// acc + the two 16-bit values of type T packed in w (v_dot2 against (1, 1):
-// the products are exact, the sum rounds once as a plain fp32 add would).
-template <int T>
-__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
-    if constexpr (T == DT_BF16)
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, 0x3f803f80u),
-                                               acc, false);
-    else
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc,
-                                      false);
-}
-
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
 // Eight ds_read_b64_tr_b16, at a[m] and at a[m] + OFF bytes (the same rows of
@@ -727,11 +706,15 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     // with a visible token moves it (its weights before that are exp2(-inf) = 0,
     // and the rescale factor exp2(kNoMax - m) is 0).
     constexpr float kNoMax = -1e30f;
-    float m_run[R], l_run[R];
+    // acc_l: the row sums of the weights, as one more 16-dim tile of P.V whose
+    // V^T is all ones (every lane of a row then holds its sum; the products
+    // are exact and the sum is kept in fp32 like the other tiles)
+    float m_run[R];
+    f32x4_t acc_l[R];
 #pragma unroll
     for (int rg = 0; rg < R; ++rg) {
         m_run[rg] = kNoMax;
-        l_run[rg] = 0.0f;
+        acc_l[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -866,7 +849,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
                 if (__builtin_amdgcn_ballot_w64(moves) != 0) {
                     const float m_new = moves ? m_blk : m_run[rg];
                     const float alpha = m_new == m_run[rg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
-                    l_run[rg] *= alpha;
+                    acc_l[rg] *= alpha;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) acc[rg][mt] *= alpha;
                     m_run[rg] = m_new;
@@ -874,10 +857,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
             }
         }
     };
-    // P = exp2(z * qscale - m) in P.V's 16-bit type.  l sums the rounded weights
-    // P.V multiplies (a normalised average of them); each lane keeps the part of
-    // its own tokens, all four lanes of a row rescale alike, and the parts are
-    // added at the end.
+    // P = exp2(z * qscale - m) in P.V's 16-bit type.
     auto softmax = [&](const float (&z)[R][8], PV (&pb)[R]) {
 #pragma unroll
         for (int rg = 0; rg < R; ++rg) {
@@ -886,12 +866,16 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
             for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(z[rg][i], qscale, -m_run[rg]));
             const uint4 pw = make_uint4(pack2<PT>(pr[0], pr[1]), pack2<PT>(pr[2], pr[3]),
                                         pack2<PT>(pr[4], pr[5]), pack2<PT>(pr[6], pr[7]));
-            l_run[rg] = add_pair<PT>(pw.w, add_pair<PT>(pw.z, add_pair<PT>(pw.y, add_pair<PT>(pw.x, l_run[rg]))));
             pb[rg] = __builtin_bit_cast(PV, pw);
         }
     };
-    // O^T += V^T . P^T over the stage's 32 tokens.
+    // O^T += V^T . P^T over the stage's 32 tokens, and the row sums of P (the
+    // weights P.V multiplies, so that the output is their normalised average).
+    const uint32_t one2 = PT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;
+    const PV ones = __builtin_bit_cast(PV, make_uint4(one2, one2, one2, one2));
     auto pv_mma = [&](const u32x2_t (&vh)[NV][8], const PV (&pb)[R]) {
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) acc_l[rg] = mma_k32<PT>(ones, pb[rg], acc_l[rg]);
         if constexpr (F8) {
 #pragma unroll
             for (int m8 = 0; m8 < MT; m8 += 8) {
@@ -989,12 +973,11 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
 
     uint16_t* o16 = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-    for (int rg = 0; rg < R; ++rg) l_run[rg] = row_sum4(l_run[rg]);
-#pragma unroll
     for (int rg = 0; rg < R; ++rg) {
         if (!live[rg]) continue;
         const int row = rg * 16 + c;
-        const float inv = l_run[rg] > 0.0f ? vscale / l_run[rg] : 0.0f;
+        const float l = acc_l[rg][0];
+        const float inv = l > 0.0f ? vscale / l : 0.0f;
         const int64_t orow = ((int64_t)(q0 + i_row[rg]) * p.H_q + hq0 + row % gs) * D;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
