@@ -359,6 +359,8 @@ def bench_prefill(args):
                                "start and end (hipExtLaunchKernel), over a second pass of the same K steps"},
         "kernel_hash": kernel_hash("paged_prefill"),
     }
+    # the plain copy kernel whose FETCH_SIZE / WRITE_SIZE calibrate the traffic counters of a run
+    result["copy_probe_GBps"] = round(copy_probe_gbs(), 1)
     result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_budget)
     print(json.dumps(result), flush=True)
 

@@ -528,22 +528,6 @@ __device__ __forceinline__ void tr_wait8(u32x2_t (&o)[8]) {
                  : "memory");
 }
 
-// A wave-uniform 32-bit read through the scalar cache.  The compiler would
-// issue it as a vector load inside the stage loop (it cannot prove the table
-// unclobbered by the LDS-bound loads) and then drain the vector counter.
-__device__ __forceinline__ int32_t scalar_read(const int32_t* ptr) {
-    int32_t v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-    return v;
-}
-// Two such reads under one wait.
-__device__ __forceinline__ void scalar_read2(const int32_t* a, const int32_t* b, int32_t& x, int32_t& y) {
-    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&s"(x), "=&s"(y)
-                 : "s"(a), "s"(b)
-                 : "memory");
-}
-
 // Direct-to-LDS loads of 16 bytes a lane (global_load_lds_dwordx4: lane l's
 // bytes land at LDS byte M0 + 16 l), written as asm.  From the builtin, the
 // compiler tracks these loads and, unable to tell which LDS bytes they write,
@@ -648,6 +632,8 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (int64_t)g * kBlock * ROWB;
     const char* zero = reinterpret_cast<const char*>(p.zero_tile);
     const int64_t blk_stride = (int64_t)p.H_kv * kBlock * ROWB;
+    const uint32_t blk_stride32 = (uint32_t)blk_stride;        // kv_heads <= 65535: below 2^28
+    const int j_whole = n / (2 * kBlock);                       // stages whose 32 tokens all lie in the context
     int ld_off[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -659,23 +645,30 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     auto lds_addr = [](const unsigned char* ptr) {     // LDS byte address of a shared-memory pointer
         return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)ptr;
     };
-    // The loads of stage jj (blocks 2 jj, 2 jj + 1) into buffer BUF = jj % 4.
-    auto issue = [&](int jj, auto BUF) {
-        // wave-uniform table reads: scalar loads, which do not count against the
-        // vector-memory counter the stage waits use
-        // Stages past the last one (jj >= n_it) keep the ring's waits uniform:
-        // they have no blocks and read the zero tile.
-        int ph0 = -1, ph1 = -1;
-        if (2 * jj + 1 < nblk) scalar_read2(table + 2 * jj, table + 2 * jj + 1, ph0, ph1);
-        else if (2 * jj < nblk) ph0 = scalar_read(table + 2 * jj);
-        const bool ok0 = ph0 >= 0 && ph0 < p.num_blocks, ok1 = ph1 >= 0 && ph1 < p.num_blocks;
-        const bool full = ok0 && ok1 && (2 * jj + 2) * kBlock <= n;          // uniform
+    // Table entries of stage jj (-1 past the visible blocks), read through the
+    // scalar cache as constant data one step before the stage's loads use them,
+    // so that their latency is not waited out at the hand-over.  Stages past
+    // the last one (jj >= n_it) keep the ring's waits uniform: they have no
+    // blocks and read the zero tile.
+    const __attribute__((address_space(4))) int32_t* ctab =
+        (const __attribute__((address_space(4))) int32_t*)table;
+    auto entries = [&](int jj, int& ph0, int& ph1) {
+        const int b0 = 2 * jj, b1 = 2 * jj + 1;
+        const int e0 = ctab[min(b0, nblk - 1)], e1 = ctab[min(b1, nblk - 1)];   // nblk >= 1 here
+        ph0 = b0 < nblk ? e0 : -1;
+        ph1 = b1 < nblk ? e1 : -1;
+    };
+    // The loads of stage jj (blocks 2 jj, 2 jj + 1, physical ph0, ph1) into
+    // buffer BUF = jj % 4.
+    auto issue = [&](int jj, auto BUF, int ph0, int ph1) {
+        const bool ok0 = (uint32_t)ph0 < (uint32_t)p.num_blocks, ok1 = (uint32_t)ph1 < (uint32_t)p.num_blocks;
+        const bool full = ok0 && ok1 && jj < j_whole;                       // uniform
         constexpr int buf = decltype(BUF)::value;
         if (full) {                            // uniform base + 32-bit lane offset
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int h = ((wave_u * NI + i) * (64 / CH)) / kBlock;      // uniform: block of this load
-                const int64_t base = (int64_t)(uint32_t)(h ? ph1 : ph0) * blk_stride;   // ph checked >= 0
+                const uint64_t base = (uint64_t)(uint32_t)(h ? ph1 : ph0) * blk_stride32;   // ph checked >= 0
                 const int dst = (wave_u * NI + i) * 64 * 16;                  // bytes
                 // a scalar base plus the lane's 32-bit offset
                 lds_dma16(kbase + base, (uint32_t)ld_off[i], lds_addr(&k_lds[buf][dst]));
@@ -722,10 +715,9 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     const int wg_min_see = p.causal ? n - q_len + tile0 : n - 1;
     // Stage jj needs masking if it reaches past the context or past the diagonal
     // of the workgroup's first query token.
-    auto stage_masked = [&](int jj) {
-        const int t0 = 2 * jj * kBlock;
-        return !(t0 + 2 * kBlock <= n && t0 + 2 * kBlock - 1 <= wg_min_see);
-    };
+    // Stage jj needs no mask iff 32 (jj + 1) <= min(n, wg_min_see + 1).
+    const int j_unmasked = max(0, min(n, wg_min_see + 1)) / (2 * kBlock);
+    auto stage_masked = [&](int jj) { return jj >= j_unmasked; };
 
     // K operand of the stage in buffer BUF, block h: token c, dims 32 k + 8 r ..
     // +7 (16 bytes, or 8 E4M3 codes widened exactly to q's type).
@@ -918,11 +910,18 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     constexpr int LPS = 2 * NI;                // loads per stage per wave
     float z[R][8];
     u32x2_t vh[NV][8];
+    int nx0 = -1, nx1 = -1;                    // table entries of the next stage to issue
     if (n_it > 0) {
-        issue(0, StageBuf<0>{});
-        issue(1, StageBuf<1>{});
-        issue(2, StageBuf<2>{});
-        issue(3, StageBuf<3>{});
+        int e0, e1;
+        entries(0, e0, e1);
+        issue(0, StageBuf<0>{}, e0, e1);
+        entries(1, e0, e1);
+        issue(1, StageBuf<1>{}, e0, e1);
+        entries(2, e0, e1);
+        issue(2, StageBuf<2>{}, e0, e1);
+        entries(3, e0, e1);
+        issue(3, StageBuf<3>{}, e0, e1);
+        entries(4, nx0, nx1);
         wait_loads_then_barrier<(kStages - 1) * LPS>();
         QV ka[2][KS];
         k_read(StageBuf<0>{}, ka);
@@ -937,7 +936,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     auto step = [&](int j, auto BUF) {
         constexpr int nbuf = (decltype(BUF)::value + 1) % kStages;
         wait_loads_then_barrier<2 * LPS>();
-        issue(j + 4, BUF);                     // (j + 4) % 4 == j % 4
+        issue(j + 4, BUF, nx0, nx1);           // (j + 4) % 4 == j % 4
         QV ka[2][KS];
         k_read(StageBuf<nbuf>{}, ka);
         PV pb[R];
@@ -949,10 +948,18 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         float zn[R][8];
         s_mma(ka, zn);
         mask(stage_masked(j + 1), j + 1, zn);  // before P.V(j), so that P.V and the maxes share a block
+        // A wave issuing P.V takes precedence over the other wave of its SIMD
+        // (which is then on its exponentials or its stage hand-over), so that
+        // the matrix cores are kept fed.
+        __builtin_amdgcn_s_setprio(1);
         pv_mma(vh, pb);
         v_issue(StageBuf<nbuf>{}, vh);         // the registers P.V(j) has just read
         row_update(zn);
         v_wait(vh);
+        __builtin_amdgcn_s_setprio(0);
+        // after the wait for the V reads: a scalar load in flight would make
+        // every LDS wait of this step wait for it too
+        entries(j + 5, nx0, nx1);
 #pragma unroll
         for (int rg = 0; rg < R; ++rg)
 #pragma unroll
