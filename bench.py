@@ -136,10 +136,10 @@ def traffic_summary(args) -> None:
            "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5),
            "calibration": f"pkv_copy of {COPY_PROBE_BYTES >> 30} GiB in the same runs: FETCH_SIZE "
                           f"{_match(fetch, 'pkv_copy'):.1f} KiB, WRITE_SIZE {_match(write, 'pkv_copy'):.1f} KiB per launch",
-           "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python -u bench.py "
-                        f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline --no-companion",
-                        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python -u bench.py "
-                        f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline --no-companion"]}
+           "commands": [f"rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python -u bench.py "
+                        f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline"
+                        + ("" if prefill else " --no-companion")
+                        for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))]}
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{args.workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
