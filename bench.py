@@ -268,11 +268,22 @@ def bench_prefill(args):
     """Multi-query attention over the paged cache: one step = kv_append of every
     sequence's chunk + paged_prefill of the chunk (queries attend causally to the
     cached tokens and to the chunk).  value = algorithmic flops / step time."""
+    w = wl.make_prefill(args.workload)
+    result = measure_prefill(w, args)
+    # the plain copy kernel whose FETCH_SIZE / WRITE_SIZE calibrate the traffic counters of a run
+    result["copy_probe_GBps"] = round(copy_probe_gbs(), 1)
+    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def measure_prefill(w, args) -> dict:
+    """Fill a pool with prefill workload w, time K steps (after W warm-ups), then
+    the same K steps again with per-kernel events.  Returns the bench record
+    without the copy probe and the CPU baseline."""
     import torch
     import harness
     import paged_kv_cache_152_amd as pkv
 
-    w = wl.make_prefill(args.workload)
     log(f"[bench] workload {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} D={w.D} "
         f"cached={w.cached} chunk={w.chunk} blocks={w.num_blocks}")
     order = np.random.default_rng(w.seed).permutation(w.num_blocks)
@@ -359,10 +370,7 @@ def bench_prefill(args):
                                "start and end (hipExtLaunchKernel), over a second pass of the same K steps"},
         "kernel_hash": kernel_hash("paged_prefill"),
     }
-    # the plain copy kernel whose FETCH_SIZE / WRITE_SIZE calibrate the traffic counters of a run
-    result["copy_probe_GBps"] = round(copy_probe_gbs(), 1)
-    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_budget)
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def cpu_baseline_prefill(w, budget_s: float = 15.0):
@@ -457,7 +465,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-companion", action="store_true",
-                    help="mha7b: skip the gqa8b figures that are otherwise measured in the same run")
+                    help="mha7b: skip the gqa8b and prefill8b figures that are otherwise measured in the same run")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the workload's traffic summary from two rocprofv3 counter runs, then exit (no GPU)")
     args = ap.parse_args()
@@ -483,6 +491,10 @@ def main():
             "decode_only_us", "kernels_us", "roofline", "partition_kernel", "config")}}
         log(f"[bench] gqa8b: {g['ms_per_step'] * 1e3:.1f} us/step, paged_decode {g['decode_only_us']:.1f} us "
             f"= {100 * g['roofline']['frac']:.1f}% of 8 TB/s")
+        # chunked prefill on the GQA shape, the matrix-core kernel (no CPU leg)
+        pf = measure_prefill(wl.make_prefill("prefill8b"), args)
+        result["companion"]["prefill8b"] = {k: pf[k] for k in (
+            "metric", "value", "unit", "ms_per_step", "flops_per_step", "kernels_us", "roofline", "config")}
     result["copy_probe_GBps"] = round(copy_probe_gbs(), 1)
     log(f"[bench] plain copy kernel: {result['copy_probe_GBps']} GB/s (read + write)")
     if not args.no_cpu_baseline:
