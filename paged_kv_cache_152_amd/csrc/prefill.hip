@@ -665,14 +665,17 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2
         const bool full = ok0 && ok1 && jj < j_whole;                       // uniform
         constexpr int buf = decltype(BUF)::value;
         if (full) {                            // uniform base + 32-bit lane offset
+            // a wave's loads cover 8 consecutive stage rows, all in one block
+            static_assert(NI * (64 / CH) <= kBlock && kBlock % (NI * (64 / CH)) == 0, "a wave's rows lie in one block");
+            const int h = (wave_u * NI * (64 / CH)) / kBlock;
+            const uint64_t base = (uint64_t)(uint32_t)(h ? ph1 : ph0) * blk_stride32;   // ph checked >= 0
+            const char* kb = kbase + base;
+            const char* vb = vbase + base;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                const int h = ((wave_u * NI + i) * (64 / CH)) / kBlock;      // uniform: block of this load
-                const uint64_t base = (uint64_t)(uint32_t)(h ? ph1 : ph0) * blk_stride32;   // ph checked >= 0
                 const int dst = (wave_u * NI + i) * 64 * 16;                  // bytes
-                // a scalar base plus the lane's 32-bit offset
-                lds_dma16(kbase + base, (uint32_t)ld_off[i], lds_addr(&k_lds[buf][dst]));
-                lds_dma16(vbase + base, (uint32_t)ld_off[i], lds_addr(&v_lds[buf][dst]));
+                lds_dma16(kb, (uint32_t)ld_off[i], lds_addr(&k_lds[buf][dst]));
+                lds_dma16(vb, (uint32_t)ld_off[i], lds_addr(&v_lds[buf][dst]));
             }
         } else {                               // rows past the context or in a bad block read the zero tile
 #pragma unroll
