@@ -149,6 +149,29 @@ __device__ __forceinline__ float row_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Loads of the cached keys and values.  With NT the nontemporal hint is set:
+// each byte is read once per call, and on this part a stream of such loads
+// runs at about 6.8 TB/s where plain loads level off near 6.0.  The hint is
+// used where one load instruction covers whole 128-byte lines, or half lines
+// whose other half the next instruction reads.  A line split over four
+// instructions (the 8-byte key loads of 1-byte pools) is fetched more than
+// once under the hint, and INT8 tiles (a header after the codes) measured
+// slower with it, so those loads stay plain.
+template <class T, bool NT = true>
+__device__ __forceinline__ T load_kv(const char* p) {
+    if constexpr (!NT) return *reinterpret_cast<const T*>(p);
+    static_assert(sizeof(T) == 16 || sizeof(T) == 8 || sizeof(T) == 4, "16-, 8- or 4-byte loads");
+    if constexpr (sizeof(T) == 16) {
+        typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const v4*>(p)));
+    } else if constexpr (sizeof(T) == 8) {
+        typedef uint32_t v2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const v2*>(p)));
+    } else {
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Pieces shared by both partition kernels.
 // ---------------------------------------------------------------------------
@@ -505,8 +528,8 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
         const int64_t off = tile + lane_off;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
-            B.k[i] = *reinterpret_cast<const RawT*>(kbase + off + i * TL::ROW);
-            B.v[i] = *reinterpret_cast<const RawT*>(vbase + off + i * TL::ROW);
+            B.k[i] = load_kv<RawT, !I8>(kbase + off + i * TL::ROW);
+            B.v[i] = load_kv<RawT, !I8>(vbase + off + i * TL::ROW);
         }
         if constexpr (I8) {
             B.kh = *reinterpret_cast<const float4*>(kbase + tile + TL::BYTES);
@@ -805,9 +828,9 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
         if (!B.ok) return;
         const int64_t off = (int64_t)phys * blk_stride + head_off;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) B.k[s] = *reinterpret_cast<const KRaw*>(kbase + off + k_off + s * 4 * TL::KW);
+        for (int s = 0; s < KS; ++s) B.k[s] = load_kv<KRaw, TL::KW == 16>(kbase + off + k_off + s * 4 * TL::KW);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) B.v[i] = *reinterpret_cast<const KRaw*>(vbase + off + v_off + i * TL::ROW);
+        for (int i = 0; i < 4; ++i) B.v[i] = load_kv<KRaw, !I8>(vbase + off + v_off + i * TL::ROW);
         if constexpr (I8) {
             B.kh = *reinterpret_cast<const float4*>(kbase + off + TL::BYTES);
             B.vh = *reinterpret_cast<const float4*>(vbase + off + TL::BYTES);
