@@ -339,7 +339,7 @@ int paged_decode(kv_pool_t* pool, const void* q, int32_t q_dtype, int32_t B, int
  * library routine.  It must be made with the pool's device current.
  *   Limit: paged_decode_workspace_bytes(pool, B, H_q, max_context_len) must
  *   not exceed PKV_NOALLOC_SCRATCH_BYTES (32 MiB: for example 64 sequences of
- *   up to 8192 tokens with 32 query heads of 128 dims need 17 MB); larger
+ *   up to 8192 tokens with 32 query heads of 128 dims need 8.5 MB); larger
  *   calls return PKV_ERR_OUT_OF_RANGE before anything is launched.
  *   Every call on one device shares that device's scratch, which keeps the
  *   last call's contents (the first kernel of a call resets what must start

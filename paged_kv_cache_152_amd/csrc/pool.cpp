@@ -785,12 +785,13 @@ int32_t resolve_partition(const kv_pool* p, int32_t B, int32_t H_q, int32_t max_
     // Contexts up to 4096 tokens with at least two (sequence, head group)
     // columns per CU run as one partition: a plain grid, no work list, no merge.
     if (max_len <= 4096 && wg_cols >= 512) return ((max_len + 63) / 64) * 64;
-    // Otherwise the largest partition in [256, 4096] that still gives >= 4096
-    // work items (about five per resident workgroup).  Multi-partition launches
-    // are scheduled longest-first from a work list, so a few long partitions do
-    // not stretch the tail, and larger partitions mean less merging.
-    int32_t P = 4096;
-    while (P > 256 && wg_cols * ((max_len + P - 1) / P) < 4096) P /= 2;
+    // Otherwise the largest partition in [256, 8192] that still gives >= 2048
+    // work items (two to three per resident workgroup).  Multi-partition
+    // launches are scheduled longest-first from a work list, so a few long
+    // partitions do not stretch the tail, and larger partitions mean fewer item
+    // start-ups and less merging.
+    int32_t P = 8192;
+    while (P > 256 && wg_cols * ((max_len + P - 1) / P) < 2048) P /= 2;
     if (max_len <= P) P = ((max_len + 63) / 64) * 64;
     return P;
 }
