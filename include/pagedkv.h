@@ -64,14 +64,15 @@ typedef struct kv_pool kv_pool_t;
 
 typedef struct {
     void* k_pool;              /* device; [num_blocks][kv_heads] tiles of block_bytes: the tile is
-                                  [block_size][head_dim] elements (INT8: codes, then a 16-byte
-                                  header {min, max, step, 0} as fp32) */
+                                  [block_size][head_dim] elements.  INT8: a block holds the
+                                  kv_heads tiles' codes ([kv_heads][block_size][head_dim]), then
+                                  their kv_heads 16-byte headers {min, max, step, 0} as fp32 */
     void* v_pool;              /* device; same layout, separate buffer */
     float* k_scale;            /* device; [kv_heads] (FP8 pools only, else NULL) */
     float* v_scale;            /* device; [kv_heads] (FP8 pools only, else NULL) */
     uint64_t pool_bytes;       /* bytes of ONE of k_pool / v_pool */
     uint64_t block_bytes;      /* bytes of one (block, kv head) tile = block_size*head_dim*elem
-                                  (+ 16 for the INT8 header) */
+                                  (+ 16 for the INT8 header); a block spans kv_heads of them */
     uint64_t total_bytes;      /* device bytes owned: 2*pool_bytes + scales + a 4 KiB zero tile
                                   (+ 8 bytes per slot of append tags for INT8 pools) */
     int32_t num_blocks, block_size, kv_heads, head_dim, dtype, elem_bytes;

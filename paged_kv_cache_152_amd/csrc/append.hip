@@ -207,9 +207,10 @@ __global__ __launch_bounds__(64) void kv_append_int8(AppendParams p) {
     const int64_t tile = tile_bytes(DT_INT8, D);
     {
         const int which = blockIdx.z;                    // 0: K, 1: V
-        uint8_t* base = reinterpret_cast<uint8_t*>(which ? p.v_pool : p.k_pool) + (blk * p.H_kv + g) * tile;
+        uint8_t* bbase = reinterpret_cast<uint8_t*>(which ? p.v_pool : p.k_pool) + blk * p.H_kv * tile;
+        uint8_t* base = bbase + (int64_t)g * kBlock * D;                 // the codes
         uint4* base4 = reinterpret_cast<uint4*>(base);
-        float* header = reinterpret_cast<float*>(base + (int64_t)kBlock * D);
+        float* header = reinterpret_cast<float*>(bbase + (int64_t)p.H_kv * kBlock * D + kInt8HeaderBytes * g);
         const void* src = which ? p.v_src : p.k_src;
         // the range of this call's values in the tile
         float lo = INFINITY, hi = -INFINITY;

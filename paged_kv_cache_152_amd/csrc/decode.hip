@@ -154,9 +154,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // runs at about 6.8 TB/s where plain loads level off near 6.0.  The hint is
 // used where one load instruction covers whole 128-byte lines, or half lines
 // whose other half the next instruction reads.  A line split over four
-// instructions (the 8-byte key loads of 1-byte pools) is fetched more than
-// once under the hint, and INT8 tiles (a header after the codes) measured
-// slower with it, so those loads stay plain.
+// instructions (the 8-byte key loads of E4M3 pools) is fetched more than once
+// under the hint, so those loads stay plain.
 template <class T, bool NT = true>
 __device__ __forceinline__ T load_kv(const char* p) {
     if constexpr (!NT) return *reinterpret_cast<const T*>(p);
@@ -507,8 +506,10 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
     const char* kbase = reinterpret_cast<const char*>(p.k_pool);
     const char* vbase = reinterpret_cast<const char*>(p.v_pool);
     const int lane_off = r * NLOAD * TL::ROW + c * TL::W;
-    const int64_t head_off = (int64_t)g * TL::STRIDE;
+    // a block holds the codes of every KV head, then (INT8) their headers
+    const int64_t head_off = (int64_t)g * TL::BYTES;
     const int64_t blk_stride = (int64_t)p.H_kv * TL::STRIDE;
+    const int64_t hdr_off = (int64_t)p.H_kv * TL::BYTES + kInt8HeaderBytes * g;
     const int blk0 = R.blk_first + wave;
     const int nmine = blk0 < R.blk_last ? (R.blk_last - blk0 + kDecodeWaves - 1) / kDecodeWaves : 0;
     WaveTable wt;
@@ -524,16 +525,16 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
         const int phys = wt.phys(j);
         B.ok = phys >= 0 && phys < p.num_blocks;
         if (!B.ok) return;
-        const int64_t tile = (int64_t)phys * blk_stride + head_off;
-        const int64_t off = tile + lane_off;
+        const int64_t blk_base = (int64_t)phys * blk_stride;
+        const int64_t off = blk_base + head_off + lane_off;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
-            B.k[i] = load_kv<RawT, !I8>(kbase + off + i * TL::ROW);
-            B.v[i] = load_kv<RawT, !I8>(vbase + off + i * TL::ROW);
+            B.k[i] = load_kv<RawT>(kbase + off + i * TL::ROW);
+            B.v[i] = load_kv<RawT>(vbase + off + i * TL::ROW);
         }
         if constexpr (I8) {
-            B.kh = *reinterpret_cast<const float4*>(kbase + tile + TL::BYTES);
-            B.vh = *reinterpret_cast<const float4*>(vbase + tile + TL::BYTES);
+            B.kh = *reinterpret_cast<const float4*>(kbase + blk_base + hdr_off);
+            B.vh = *reinterpret_cast<const float4*>(vbase + blk_base + hdr_off);
         }
     };
     auto update = [&](auto masked, int blk, const Buf& B) {
@@ -768,15 +769,19 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
     }
     if (part >= R.nparts) return;
 
-    // B operand: head c (zero beyond GS), dims 8 * (4 s + r) .. +7 for step s.
+    // B operand: head c (zero beyond GS), for step s dims 8 (4 s + r) .. +7, or
+    // for INT8 keys 32 r + 8 s .. +7 (a lane then reads its keys as two 16-byte
+    // runs).  Q.K^T sums over all dims either way.
+    constexpr bool KRUN = KDT == DT_INT8;
     MT qb[KS];
     {
         const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+            const int d0 = KRUN ? 32 * r + 8 * s : 8 * (4 * s + r);
             if (c < GS)
-                raw = *reinterpret_cast<const uint4*>(q16 + ((int64_t)b * p.H_q + hq0 + c) * D + 8 * (4 * s + r));
+                raw = *reinterpret_cast<const uint4*>(q16 + ((int64_t)b * p.H_q + hq0 + c) * D + d0);
             qb[s] = __builtin_bit_cast(MT, raw);
         }
     }
@@ -805,10 +810,13 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
     const int32_t* table = p.tables + (int64_t)b * p.max_blocks;
     const char* kbase = reinterpret_cast<const char*>(p.k_pool);
     const char* vbase = reinterpret_cast<const char*>(p.v_pool);
-    const int64_t head_off = (int64_t)g * TL::STRIDE;
+    // a block holds the codes of every KV head, then (INT8) their headers
+    const int64_t head_off = (int64_t)g * TL::BYTES;
     const int64_t blk_stride = (int64_t)p.H_kv * TL::STRIDE;
-    // K: token c, step s -> bytes KW * (4 s + r); V: token 4 r + i, bytes KW * c.
-    const int k_off = c * TL::ROW + r * TL::KW;
+    const int64_t hdr_off = (int64_t)p.H_kv * TL::BYTES + kInt8HeaderBytes * g;
+    // K: token c, step s -> bytes KW (4 s + r), or 32 r + 8 s for INT8;
+    // V: token 4 r + i, bytes KW c.
+    const int k_off = c * TL::ROW + (KRUN ? 32 * r : r * TL::KW);
     const int v_off = (4 * r) * TL::ROW + c * TL::KW;
     const int blk0 = R.blk_first + wave;
     const int nmine = blk0 < R.blk_last ? (R.blk_last - blk0 + kDecodeWaves - 1) / kDecodeWaves : 0;
@@ -826,14 +834,24 @@ __device__ __forceinline__ void gqa_item(const DecodeParams& p, int b, int part,
         const int phys = wt.phys(j);
         B.ok = phys >= 0 && phys < p.num_blocks;
         if (!B.ok) return;
-        const int64_t off = (int64_t)phys * blk_stride + head_off;
+        const int64_t blk_base = (int64_t)phys * blk_stride;
+        const int64_t off = blk_base + head_off;
+        if constexpr (KRUN) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) B.k[s] = load_kv<KRaw, TL::KW == 16>(kbase + off + k_off + s * 4 * TL::KW);
+            for (int s2 = 0; s2 < KS / 2; ++s2) {
+                const uint4 w = load_kv<uint4>(kbase + off + k_off + 16 * s2);
+                B.k[2 * s2] = make_uint2(w.x, w.y);
+                B.k[2 * s2 + 1] = make_uint2(w.z, w.w);
+            }
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) B.v[i] = load_kv<KRaw, !I8>(vbase + off + v_off + i * TL::ROW);
+            for (int s = 0; s < KS; ++s) B.k[s] = load_kv<KRaw, TL::KW == 16>(kbase + off + k_off + s * 4 * TL::KW);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) B.v[i] = load_kv<KRaw>(vbase + off + v_off + i * TL::ROW);
         if constexpr (I8) {
-            B.kh = *reinterpret_cast<const float4*>(kbase + off + TL::BYTES);
-            B.vh = *reinterpret_cast<const float4*>(vbase + off + TL::BYTES);
+            B.kh = *reinterpret_cast<const float4*>(kbase + blk_base + hdr_off);
+            B.vh = *reinterpret_cast<const float4*>(vbase + blk_base + hdr_off);
         }
     };
     auto update = [&](auto masked, int blk, const Buf& B) {

@@ -17,7 +17,12 @@ enum Dt : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_INT8 = 4
 
 __host__ __device__ inline int elem_bytes(int32_t dt) { return dt == DT_F32 ? 4 : (dt == DT_FP8 || dt == DT_INT8 ? 1 : 2); }
 
-// INT8 min-max tiles end in a 16-byte header {min, max, step = (max - min) / 255, 0}.
+// INT8 min-max tiles carry a 16-byte header {min, max, step = (max - min) / 255, 0}.
+// A block of an INT8 pool holds the codes of its kv_heads tiles first
+// (kBlock * D bytes each, so every tile's rows stay on 128-byte lines when
+// kv_heads is a multiple of 8), then the kv_heads headers: tile (blk, g) has
+// its codes at blk * kv_heads * tile_bytes + g * kBlock * D and its header at
+// blk * kv_heads * tile_bytes + kv_heads * kBlock * D + 16 g.
 constexpr int kInt8HeaderBytes = 16;
 
 // Bytes of one (block, KV head) tile of a pool.

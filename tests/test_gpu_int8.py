@@ -91,9 +91,11 @@ class Int8Case:
                     blk = int(tables[s, j])
                     rows = min(16, int(n) - 16 * j)
                     for g in range(self.H_kv):
-                        t0 = (blk * self.H_kv + g) * tb
+                        b0 = blk * self.H_kv * tb              # the block: every head's codes, then the headers
+                        t0 = b0 + g * 16 * self.D
+                        h0 = b0 + self.H_kv * 16 * self.D + 16 * g
                         codes = raw[t0:t0 + 16 * self.D].reshape(16, self.D)
-                        header = raw[t0 + 16 * self.D:t0 + tb].view(np.float32)
+                        header = raw[h0:h0 + 16].view(np.float32)
                         want_codes, (lo, hi) = self.model.tile(kind, blk, g)
                         assert np.array_equal(codes[:rows], want_codes[:rows]), (kind, s, j, g)
                         assert header[0] == lo and header[1] == hi, (kind, s, j, g, header[:2], lo, hi)
