@@ -212,6 +212,41 @@ def copy_probe_gbs(nbytes: int = 2 << 30, reps: int = 10) -> float:
     return 2 * nbytes / float(np.median(times)) / 1e9
 
 
+def read_probe_gbs(nbytes: int = 2 << 30, reps: int = 10, fill: str = "normal_f16") -> dict:
+    """HBM read rate of a streaming read (pkv_read_probe, 16-byte loads in 16 KiB
+    runs per workgroup), plain and with the nontemporal hint: bytes read / time,
+    median of `reps` passes each (one event pair per pass).  The rate depends on
+    the bytes read, so `fill` picks them: "normal_f16" (seeded N(0,1) half
+    floats, what the fp16 decode workloads cache), "uniform_u8" (seeded uniform
+    random bytes) or "constant" (every byte 0x01)."""
+    import torch
+    import paged_kv_cache_152_amd as pkv
+    g = torch.Generator(device="cuda").manual_seed(1)
+    if fill == "normal_f16":
+        src = torch.randn(nbytes // 2, dtype=torch.float16, device="cuda", generator=g).view(torch.uint8)
+    elif fill == "uniform_u8":
+        src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    elif fill == "constant":
+        src = torch.full((nbytes,), 1, dtype=torch.uint8, device="cuda")
+    else:
+        raise ValueError(f"unknown fill {fill!r}")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, nt in (("plain", False), ("nontemporal", True)):
+        pkv.read_probe(src, sink, nt)
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            pkv.read_probe(src, sink, nt)
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        out[name] = round(nbytes / float(np.median(times)) / 1e9, 1)
+    del src, sink
+    return out
+
+
 def cpu_baseline(w: wl.Workload, budget_s: float = 15.0):
     """The fp64 oracle on a bounded sample of the same workload, timed on the host.
 
@@ -466,6 +501,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-companion", action="store_true",
                     help="mha7b: skip the gqa8b and prefill8b figures that are otherwise measured in the same run")
+    ap.add_argument("--probes-only", action="store_true",
+                    help="time only the copy probe and the streaming-read probe (2 GiB, three fills) and print them")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the workload's traffic summary from two rocprofv3 counter runs, then exit (no GPU)")
     args = ap.parse_args()
@@ -476,6 +513,10 @@ def main():
               "(each GPU would own its own pool and sequences); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.probes_only:
+        reads = {f: read_probe_gbs(fill=f) for f in ("normal_f16", "uniform_u8", "constant")}
+        print(json.dumps({"copy_probe_GBps": round(copy_probe_gbs(), 1), "read_probe_GBps": reads}), flush=True)
+        return
     if args.workload.startswith("prefill"):
         return bench_prefill(args)
     if args.workload == "swap":
@@ -497,6 +538,9 @@ def main():
             "metric", "value", "unit", "ms_per_step", "flops_per_step", "kernels_us", "roofline", "config")}
     result["copy_probe_GBps"] = round(copy_probe_gbs(), 1)
     log(f"[bench] plain copy kernel: {result['copy_probe_GBps']} GB/s (read + write)")
+    result["read_probe_GBps"] = read_probe_gbs()
+    log(f"[bench] streaming read: {result['read_probe_GBps']['plain']} GB/s plain, "
+        f"{result['read_probe_GBps']['nontemporal']} GB/s nontemporal")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -466,6 +466,17 @@ int pkv_profile_read(kv_pool_t* pool, pkv_kernel_stat_t* out, int32_t cap, int32
  * Errors: INVALID_ARG, DEVICE. */
 int pkv_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* Read-only streaming probe over `bytes` of device memory at `src` (a multiple
+ * of 16, 16-byte aligned): 16-byte loads, each workgroup taking 16 KiB runs,
+ * with the nontemporal hint when `nontemporal` is 1 and plain loads when 0.
+ * It measures the HBM read rate the decode kernels' loads can reach.  The
+ * launch XORs the XOR of all 32-bit words of the buffer into *sink (a device
+ * uint32, 4-byte aligned, owned by the caller; zero it first to read the
+ * checksum).  Asynchronous on stream; bytes == 0 launches nothing (src may
+ * then be NULL).
+ * Errors: INVALID_ARG, DEVICE. */
+int pkv_read_probe(const void* src, size_t bytes, int32_t nontemporal, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -103,6 +103,7 @@ _SIGNATURES = {
     "pkv_profile_enable": (ctypes.c_int, [_P, _I32]),
     "pkv_profile_read": (ctypes.c_int, [_P, ctypes.POINTER(KernelStat), _I32, _PI32]),
     "pkv_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    "pkv_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _P, _P]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -479,6 +480,15 @@ def copy(dst, src, stream=None) -> None:
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("size mismatch")
     _check(lib().pkv_copy(_dev(dst, "dst"), _dev(src, "src"), nbytes, _stream(stream)), "pkv_copy")
+
+
+def read_probe(src, sink, nontemporal: bool, stream=None) -> None:
+    """pkv_read_probe: stream-read src (plain or nontemporal 16-byte loads) and
+    XOR the XOR of its 32-bit words into sink (a device int32 tensor of one
+    element)."""
+    torch = _torch()
+    _check(lib().pkv_read_probe(_dev(src, "src"), src.numel() * src.element_size(), int(bool(nontemporal)),
+                                _dev(sink, "sink", torch.int32, (1,)), _stream(stream)), "pkv_read_probe")
 
 
 # C-ABI names as plain functions over a KVPool.

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["pool.cpp", "decode.hip", "append.hip", "prefill.hip"]
+SOURCES = ["pool.cpp", "decode.hip", "append.hip", "prefill.hip", "probe.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

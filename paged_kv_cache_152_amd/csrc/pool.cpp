@@ -1216,6 +1216,16 @@ int pkv_copy(void* dst, const void* src, size_t bytes, void* stream) {
     return ok();
 }
 
+int pkv_read_probe(const void* src, size_t bytes, int32_t nontemporal, uint32_t* sink, void* stream) {
+    if ((!src && bytes) || !sink) return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+    if (bytes % 16 || !aligned16(src)) return fail(PKV_ERR_INVALID_ARG, "read probe needs 16-byte granularity");
+    if (reinterpret_cast<uintptr_t>(sink) % 4) return fail(PKV_ERR_INVALID_ARG, "sink must be 4-byte aligned");
+    if (nontemporal != 0 && nontemporal != 1) return fail(PKV_ERR_INVALID_ARG, "nontemporal must be 0 or 1");
+    hipError_t e = pkv::launch_read_probe(src, bytes, nontemporal == 1, sink, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "read probe launch");
+    return ok();
+}
+
 }  // extern "C"
 
 namespace pkv {
