@@ -213,12 +213,17 @@ def copy_probe_gbs(nbytes: int = 2 << 30, reps: int = 10) -> float:
 
 
 def read_probe_gbs(nbytes: int = 2 << 30, reps: int = 10, fill: str = "normal_f16") -> dict:
-    """HBM read rate of a streaming read (pkv_read_probe, 16-byte loads in 16 KiB
-    runs per workgroup), plain and with the nontemporal hint: bytes read / time,
-    median of `reps` passes each (one event pair per pass).  The rate depends on
-    the bytes read, so `fill` picks them: "normal_f16" (seeded N(0,1) half
-    floats, what the fp16 decode workloads cache), "uniform_u8" (seeded uniform
-    random bytes) or "constant" (every byte 0x01)."""
+    """HBM read rate of pkv_read_probe (16-byte loads, four or, gathered, eight
+    4 KiB loads in flight per workgroup, two workgroups per CU), plain and with
+    the nontemporal hint:
+    bytes read / time, median of `reps` passes each (one event pair per pass).
+    "plain" / "nontemporal" read the buffer in address order; "gather_4KiB" and
+    "gather_32KiB" read it in chunks of that size in a seeded random order, as
+    the decode kernels read their tiles (one KV head's 16-token tile of a
+    128-dim 16-bit cache is 4 KiB; one block of eight such heads is 32 KiB).
+    The rate depends on the bytes read, so `fill` picks them: "normal_f16"
+    (seeded N(0,1) half floats, what the fp16 decode workloads cache),
+    "uniform_u8" (seeded uniform random bytes) or "constant" (every byte 0x01)."""
     import torch
     import paged_kv_cache_152_amd as pkv
     g = torch.Generator(device="cuda").manual_seed(1)
@@ -231,19 +236,25 @@ def read_probe_gbs(nbytes: int = 2 << 30, reps: int = 10, fill: str = "normal_f1
     else:
         raise ValueError(f"unknown fill {fill!r}")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    orders = {c: torch.from_numpy(np.random.default_rng(c).permutation(nbytes // c).astype(np.int32)).cuda()
+              for c in (4096, 32768)}
+    cases = [("plain", False, None), ("nontemporal", True, None)]
+    for c in (4096, 32768):
+        cases += [(f"gather_{c // 1024}KiB_plain", False, c), (f"gather_{c // 1024}KiB_nontemporal", True, c)]
     out = {}
-    for name, nt in (("plain", False), ("nontemporal", True)):
-        pkv.read_probe(src, sink, nt)
+    for name, nt, chunk in cases:
+        kw = {} if chunk is None else {"order": orders[chunk], "chunk_bytes": chunk}
+        pkv.read_probe(src, sink, nt, **kw)
         times = []
         for _ in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            pkv.read_probe(src, sink, nt)
+            pkv.read_probe(src, sink, nt, **kw)
             b.record()
             b.synchronize()
             times.append(a.elapsed_time(b) * 1e-3)
         out[name] = round(nbytes / float(np.median(times)) / 1e9, 1)
-    del src, sink
+    del src, sink, orders
     return out
 
 
@@ -539,8 +550,7 @@ def main():
     result["copy_probe_GBps"] = round(copy_probe_gbs(), 1)
     log(f"[bench] plain copy kernel: {result['copy_probe_GBps']} GB/s (read + write)")
     result["read_probe_GBps"] = read_probe_gbs()
-    log(f"[bench] streaming read: {result['read_probe_GBps']['plain']} GB/s plain, "
-        f"{result['read_probe_GBps']['nontemporal']} GB/s nontemporal")
+    log(f"[bench] read probe (GB/s): {result['read_probe_GBps']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

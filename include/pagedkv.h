@@ -466,16 +466,26 @@ int pkv_profile_read(kv_pool_t* pool, pkv_kernel_stat_t* out, int32_t cap, int32
  * Errors: INVALID_ARG, DEVICE. */
 int pkv_copy(void* dst, const void* src, size_t bytes, void* stream);
 
-/* Read-only streaming probe over `bytes` of device memory at `src` (a multiple
- * of 16, 16-byte aligned): 16-byte loads, each workgroup taking 16 KiB runs,
- * with the nontemporal hint when `nontemporal` is 1 and plain loads when 0.
- * It measures the HBM read rate the decode kernels' loads can reach.  The
- * launch XORs the XOR of all 32-bit words of the buffer into *sink (a device
+/* Read-only probe over `bytes` of device memory at `src` (a multiple of 16,
+ * 16-byte aligned): 16-byte loads, every wave instruction over 1 KiB, 512
+ * workgroups each with four (address order) or eight (gathered) 4 KiB loads
+ * in flight, with the nontemporal hint
+ * when `nontemporal` is 1 and plain loads when 0.  It measures the HBM read
+ * rate the decode kernels' loads can reach.
+ *   order == NULL: the whole buffer in address order (n_order and
+ *     chunk_bytes are ignored).
+ *   order != NULL: a device array of n_order int32 chunk indices, owned by
+ *     the caller; the buffer is cut into chunks of chunk_bytes (4096 times a
+ *     power of two, dividing bytes) and the chunks are read in list order,
+ *     as the paged kernels read tiles through a block table.  Entries outside
+ *     [0, bytes / chunk_bytes) are skipped.
+ * The launch XORs the XOR of all 32-bit words it read into *sink (a device
  * uint32, 4-byte aligned, owned by the caller; zero it first to read the
- * checksum).  Asynchronous on stream; bytes == 0 launches nothing (src may
- * then be NULL).
+ * checksum).  Asynchronous on stream; nothing to read launches nothing (src
+ * may then be NULL).
  * Errors: INVALID_ARG, DEVICE. */
-int pkv_read_probe(const void* src, size_t bytes, int32_t nontemporal, uint32_t* sink, void* stream);
+int pkv_read_probe(const void* src, size_t bytes, int32_t nontemporal, const int32_t* order, int64_t n_order,
+                   int32_t chunk_bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -103,7 +103,7 @@ _SIGNATURES = {
     "pkv_profile_enable": (ctypes.c_int, [_P, _I32]),
     "pkv_profile_read": (ctypes.c_int, [_P, ctypes.POINTER(KernelStat), _I32, _PI32]),
     "pkv_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
-    "pkv_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _P, _P]),
+    "pkv_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _P, ctypes.c_int64, _I32, _P, _P]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -482,13 +482,19 @@ def copy(dst, src, stream=None) -> None:
     _check(lib().pkv_copy(_dev(dst, "dst"), _dev(src, "src"), nbytes, _stream(stream)), "pkv_copy")
 
 
-def read_probe(src, sink, nontemporal: bool, stream=None) -> None:
-    """pkv_read_probe: stream-read src (plain or nontemporal 16-byte loads) and
-    XOR the XOR of its 32-bit words into sink (a device int32 tensor of one
-    element)."""
+def read_probe(src, sink, nontemporal: bool, order=None, chunk_bytes: int = 0, stream=None) -> None:
+    """pkv_read_probe: read src (plain or nontemporal 16-byte loads), in address
+    order, or chunk by chunk in the order of the device int32 tensor `order`
+    (chunks of chunk_bytes), and XOR the XOR of the 32-bit words read into
+    sink (a device int32 tensor of one element)."""
     torch = _torch()
+    if order is None:
+        optr, n_order = None, 0
+    else:
+        optr, n_order = _dev(order, "order", torch.int32), order.numel()
     _check(lib().pkv_read_probe(_dev(src, "src"), src.numel() * src.element_size(), int(bool(nontemporal)),
-                                _dev(sink, "sink", torch.int32, (1,)), _stream(stream)), "pkv_read_probe")
+                                optr, n_order, int(chunk_bytes), _dev(sink, "sink", torch.int32, (1,)),
+                                _stream(stream)), "pkv_read_probe")
 
 
 # C-ABI names as plain functions over a KVPool.

@@ -140,6 +140,8 @@ constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 hipError_t noalloc_scratch(int device, void** ptr);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_read_probe(const void* src, size_t bytes, bool nontemporal, uint32_t* sink, hipStream_t stream);
+hipError_t launch_gather_read_probe(const void* src, size_t bytes, bool nontemporal, const int32_t* order,
+                                    int64_t n_order, int log_rows, uint32_t* sink, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 hipError_t launch_move_blocks(const MoveParams& p, hipStream_t stream);
 bool prefill_supported(int32_t kv_dt, int32_t q_dt, int32_t D);

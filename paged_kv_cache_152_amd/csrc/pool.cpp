@@ -1216,12 +1216,27 @@ int pkv_copy(void* dst, const void* src, size_t bytes, void* stream) {
     return ok();
 }
 
-int pkv_read_probe(const void* src, size_t bytes, int32_t nontemporal, uint32_t* sink, void* stream) {
+int pkv_read_probe(const void* src, size_t bytes, int32_t nontemporal, const int32_t* order, int64_t n_order,
+                   int32_t chunk_bytes, uint32_t* sink, void* stream) {
     if ((!src && bytes) || !sink) return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
     if (bytes % 16 || !aligned16(src)) return fail(PKV_ERR_INVALID_ARG, "read probe needs 16-byte granularity");
     if (reinterpret_cast<uintptr_t>(sink) % 4) return fail(PKV_ERR_INVALID_ARG, "sink must be 4-byte aligned");
     if (nontemporal != 0 && nontemporal != 1) return fail(PKV_ERR_INVALID_ARG, "nontemporal must be 0 or 1");
-    hipError_t e = pkv::launch_read_probe(src, bytes, nontemporal == 1, sink, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (!order) {
+        e = pkv::launch_read_probe(src, bytes, nontemporal == 1, sink, st);
+    } else {
+        if (n_order < 0) return fail(PKV_ERR_INVALID_ARG, "n_order must be >= 0");
+        if (reinterpret_cast<uintptr_t>(order) % 4) return fail(PKV_ERR_INVALID_ARG, "order must be 4-byte aligned");
+        int log_rows = -1;
+        for (int k = 0; k <= 18; ++k)
+            if (chunk_bytes == (4096 << k)) log_rows = k;
+        if (log_rows < 0) return fail(PKV_ERR_INVALID_ARG, "chunk_bytes must be 4096 times a power of two, at most 1 GiB");
+        if (bytes % (size_t)chunk_bytes) return fail(PKV_ERR_INVALID_ARG, "bytes must be a multiple of chunk_bytes");
+        if (n_order > (INT64_MAX >> (log_rows + 1))) return fail(PKV_ERR_INVALID_ARG, "n_order too large");
+        e = pkv::launch_gather_read_probe(src, bytes, nontemporal == 1, order, n_order, log_rows, sink, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "read probe launch");
     return ok();
 }
