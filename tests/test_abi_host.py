@@ -315,6 +315,31 @@ def test_device_calls_validate_before_device_work():
     p.close()
 
 
+def test_probes_validate_before_device_work():
+    """pkv_copy and pkv_read_probe refuse bad arguments on the host, before any
+    launch (the pointers below are never dereferenced)."""
+    L = pkv.lib()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+    assert L.pkv_copy(None, fake, 64, None) == pkv.ERR_INVALID_ARG
+    assert L.pkv_copy(fake, fake, 24, None) == pkv.ERR_INVALID_ARG          # not a multiple of 16
+    assert L.pkv_copy(odd, fake, 64, None) == pkv.ERR_INVALID_ARG           # misaligned
+    rp = lambda **kw: L.pkv_read_probe(kw.get("src", fake), kw.get("n", 1 << 20), kw.get("nt", 1),
+                                       kw.get("order", None), kw.get("no", 0), kw.get("cb", 0),
+                                       kw.get("sink", fake), None)
+    assert rp(src=None) == pkv.ERR_INVALID_ARG
+    assert rp(sink=None) == pkv.ERR_INVALID_ARG
+    assert rp(n=24) == pkv.ERR_INVALID_ARG
+    assert rp(src=odd) == pkv.ERR_INVALID_ARG
+    assert rp(sink=ctypes.c_void_p(0x10002)) == pkv.ERR_INVALID_ARG
+    assert rp(nt=2) == pkv.ERR_INVALID_ARG
+    for cb in (0, -4096, 2048, 3 * 4096):                                      # not 4096 x 2^k
+        assert rp(order=fake, no=4, cb=cb) == pkv.ERR_INVALID_ARG
+    assert rp(order=fake, no=4, cb=1 << 21) == pkv.ERR_INVALID_ARG          # 1 MiB buffer, 2 MiB chunks
+    assert rp(order=fake, no=-1, cb=4096) == pkv.ERR_INVALID_ARG
+    assert rp(order=ctypes.c_void_p(0x10002), no=4, cb=4096) == pkv.ERR_INVALID_ARG
+
+
 def test_decode_noalloc_validates_and_bounds_its_scratch():
     """paged_decode_noalloc: the same argument checks as paged_decode; sizes whose
     workspace exceeds the fixed scratch are refused with OUT_OF_RANGE before any
