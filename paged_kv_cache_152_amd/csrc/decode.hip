@@ -298,13 +298,23 @@ __device__ __forceinline__ void pipeline(int nmine, Fetch&& fetch, Consume&& con
 //
 // Planned mode: kernel 0 (paged_decode_plan) lists the live (sequence,
 // partition) items longest first, and the partition kernel runs a grid only
-// as large as the GPU holds at once.  Each workgroup takes item blockIdx.x,
-// then further items from an atomic counter, until the list is exhausted:
+// as large as the GPU holds at once.  Each workgroup takes one of the first
+// gridDim.x items (first_ticket), then further items from an atomic counter,
+// until the list is exhausted:
 // long partitions start first and short ones fill the tail.  Items are
 // expanded over head groups (consecutive virtual items share a partition, so
 // the heads of one block are read close together in time).  Which workgroup
 // computes an item has no influence on the bits it produces.
 // ---------------------------------------------------------------------------
+// First ticket of workgroup i of n: workgroups are dealt round-robin over the
+// 8 XCDs, so workgroup i takes ticket (i % 8) * (n / 8) + i / 8, and the head
+// groups of one (sequence, partition), consecutive tickets, share an XCD and
+// its L2 (the INT8 headers of a block sit on one line for all heads).
+__device__ __forceinline__ int first_ticket(int i, int n) {
+    const int full = n - n % 8;
+    return i >= full ? i : (i % 8) * (full / 8) + i / 8;
+}
+
 template <class F>
 __device__ __forceinline__ void for_each_item(const DecodeParams& p, F&& f) {
     __shared__ int s_next;
@@ -312,7 +322,7 @@ __device__ __forceinline__ void for_each_item(const DecodeParams& p, F&& f) {
     const int HG = p.head_groups;
     const int total = planned ? p.sched[kSchedItems] * HG : 1;
     const int P = part_tokens(p);
-    int v = planned ? (int)blockIdx.x : 0;
+    int v = planned ? first_ticket((int)blockIdx.x, (int)gridDim.x) : 0;
     while (v < total) {                        // one call site, so the item body is inlined
         int b, part, hgi;
         if (planned) {
