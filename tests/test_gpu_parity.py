@@ -485,6 +485,25 @@ def test_full_size_config_every_sequence(name):
     assert raw == r["raw_max_abs"]
 
 
+@pytest.mark.parametrize("partition", [0, 256])
+def test_very_long_context(partition):
+    """One sequence of 262,144 tokens (GQA 32/8, bf16; 1 GiB of K/V) beside two
+    short ones: the automatic partition and 256-token partitions (1024 of them,
+    the merge's general loop), every output against the oracle."""
+    w = wl.custom(91, [262144, 17, 3000], 32, 8, 128, wl.BF16)
+    w.cache_kv = True
+    say(f"[test] very long context, partition {partition}: {w.num_blocks} blocks")
+    prep = harness.prepare(w, partition_tokens=partition)
+    out = prep.step()
+    torch.cuda.synchronize()
+    got = harness.out_to_f64(out)
+    prep.pool.close()
+    want = expected(w)
+    w._kv_cache.clear()
+    err = assert_close(got, want, wl.BF16, f"262144 tokens P={partition}")
+    say(f"very long context P={partition}: raw max-abs {err:.2e}")
+
+
 # ------------------------------------------------------------------ closed forms
 # softmax(s q K^T) V (www.mlqm.cn/news/394450, section 二) in cases where the
 # result has a form of its own: s = 0 or q = 0 weighs every token equally (the
