@@ -222,6 +222,27 @@ def test_prefill_long_context_sampled(kv_dt):
     c.close()
 
 
+@pytest.mark.parametrize("kv_dt", [wl.BF16, wl.E4M3])
+def test_prefill_very_long_context_sampled(kv_dt):
+    """A 256-token chunk after 65,280 cached tokens (4080 blocks, 2048 stages
+    for the last query tile) beside a short sequence: sampled rows against the
+    oracle."""
+    c = Case(kv_dt, 32, 8, 128, [(65536, 256), (300, 45)], seed=13)
+    got = c.run()
+    K, V = c.oracle_kv()
+    kw = dict(k_scale=c.scales[0], v_scale=c.scales[1]) if c.scales else {}
+    off = [0, int(c.lens[0])]
+    rows = [0, 127, 128, 255, 256, 300]
+    for t in rows:
+        s = 0 if t < c.q_start[1] else 1
+        i = t - c.q_start[s]
+        p = int(c.lens[s]) - int(c.q_lens[s]) + i
+        want = oracle.prefill_attention(c.q[t:t + 1], c.q_dt, [0, 1], K, V, kv_dt, [off[s]], [p + 1],
+                                        c.scale, **kw)
+        check(got[t:t + 1], want, kv_dt, c.q_dt, f"row {t}")
+    c.close()
+
+
 @pytest.mark.parametrize("scale", [-0.09, 0.0])
 @pytest.mark.parametrize("kv_dt", [wl.BF16, wl.E4M3])
 def test_prefill_scale_sign(scale, kv_dt):
