@@ -290,6 +290,50 @@ __device__ __forceinline__ void pipeline(int nmine, Fetch&& fetch, Consume&& con
     }
 }
 
+// The vector kernel's variant of the two helpers above.  The wave's block ids
+// come from scalar loads one block ahead (take(j) returns block j's id, loaded
+// during take(j - 1), and starts the load of block j + 1's; past the wave's
+// last block it returns -1), and every step fetches, also past the last block
+// (fetch then reads block 0 and marks it absent).  With no load behind a
+// branch the compiler counts the loads in flight and waits for block j's alone
+// before consuming it.  On the matrix-core kernel the same change measured
+// slower (table entries through the scalar cache stall its waves); on the
+// vector kernel it is faster.
+struct ScalarWaveTable {
+    const __attribute__((address_space(4))) int32_t* row = nullptr;
+    int blk0 = 0, nmine = 0, next = -1;
+    __device__ __forceinline__ int entry(int j) const {
+        return nmine > 0 ? row[blk0 + kDecodeWaves * min(j, nmine - 1)] : -1;
+    }
+    __device__ __forceinline__ void init(const int32_t* table, int blk0_, int nmine_) {
+        row = (const __attribute__((address_space(4))) int32_t*)table;
+        blk0 = blk0_;
+        nmine = nmine_;
+        next = entry(0);
+    }
+    __device__ __forceinline__ int take(int j) {
+        const int cur = j < nmine ? next : -1;
+        next = entry(j + 1);
+        return cur;
+    }
+};
+
+template <int NB, class Buf, class Fetch, class Consume>
+__device__ __forceinline__ void pipeline_all(int nmine, Fetch&& fetch, Consume&& consume) {
+    Buf ring[NB];
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k) fetch(k, ring[k]);
+    for (int j0 = 0; j0 < nmine; j0 += NB) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int j = j0 + k;
+            if (j >= nmine) return;
+            fetch(j + NB - 1, ring[(k + NB - 1) % NB]);
+            consume(j, ring[k]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Work distribution.
 //
@@ -520,10 +564,10 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
     const int64_t head_off = (int64_t)g * TL::BYTES;
     const int64_t blk_stride = (int64_t)p.H_kv * TL::STRIDE;
     const int64_t hdr_off = (int64_t)p.H_kv * TL::BYTES + kInt8HeaderBytes * g;
-    const int blk0 = R.blk_first + wave;
+    const int blk0 = R.blk_first + __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar table loads
     const int nmine = blk0 < R.blk_last ? (R.blk_last - blk0 + kDecodeWaves - 1) / kDecodeWaves : 0;
-    WaveTable wt;
-    wt.load(table, blk0, nmine, 0, lane);
+    ScalarWaveTable wt;
+    wt.init(table, blk0, nmine);
 
     struct Buf {
         RawT k[NLOAD], v[NLOAD];
@@ -531,11 +575,9 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
         bool ok;
     };
     auto fetch = [&](int j, Buf& B) {
-        if ((j & 63) == 0 && j > 0) wt.load(table, blk0, nmine, j, lane);
-        const int phys = wt.phys(j);
+        const int phys = wt.take(j);
         B.ok = phys >= 0 && phys < p.num_blocks;
-        if (!B.ok) return;
-        const int64_t blk_base = (int64_t)phys * blk_stride;
+        const int64_t blk_base = (int64_t)(B.ok ? phys : 0) * blk_stride;   // absent: block 0, unused
         const int64_t off = blk_base + head_off + lane_off;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
@@ -609,7 +651,7 @@ __device__ __forceinline__ void vec_item(const DecodeParams& p, int b, int part,
         if (blk * kBlock + kBlock > R.pend) update(std::integral_constant<bool, true>{}, blk, B);
         else update(std::integral_constant<bool, false>{}, blk, B);
     };
-    pipeline<2, Buf>(nmine, fetch, consume);
+    pipeline_all<2, Buf>(nmine, fetch, consume);
 
     const int s = wave * RPL + r;
 #pragma unroll
